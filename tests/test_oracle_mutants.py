@@ -1,0 +1,143 @@
+"""Test of the tests: each plausible mistake planted in the oracle (on the CPU, through
+monkeypatch) must make at least one pin in test_oracle_pins fail."""
+import numpy as np
+import pytest
+
+import tests.test_oracle_pins as pins
+from oracle import hc_oracle as o
+
+_real_sinkhorn = o.sinkhorn
+_real_stats = o.hc_mix_stats
+_real_split = o.hc_split
+_real_combine_norm = o.hc_combine_norm
+_real_post = o.hc_post
+_real_e4m3 = o.e4m3_encode
+_real_scale_exp = o.mxfp8_scale_exponent
+
+
+def _sinkhorn_row_last(L, iters=20, eps=1e-6):
+    P = np.exp(L - L.max(-1, keepdims=True))
+    P = P / P.sum(-1, keepdims=True) + eps
+    for _ in range(iters):
+        P = P / (P.sum(-2, keepdims=True) + eps)
+        P = P / (P.sum(-1, keepdims=True) + eps)
+    return P
+
+
+def _sinkhorn_one_round_short(L, iters=20, eps=1e-6):
+    return _real_sinkhorn(L, max(iters - 1, 1), eps)
+
+
+def _sinkhorn_eps_only_in_denominators(L, iters=20, eps=1e-6):
+    P = np.exp(L - L.max(-1, keepdims=True))
+    P = P / P.sum(-1, keepdims=True)
+    P = P / (P.sum(-2, keepdims=True) + eps)
+    for _ in range(iters - 1):
+        P = P / (P.sum(-1, keepdims=True) + eps)
+        P = P / (P.sum(-2, keepdims=True) + eps)
+    return P
+
+
+def _sinkhorn_transposed(L, iters=20, eps=1e-6):
+    return np.swapaxes(_real_sinkhorn(np.swapaxes(L, -1, -2), iters, eps), -1, -2)
+
+
+def _stats_h_major(R_bits, fn, rms_eps=1e-6):
+    R_bits = np.asarray(R_bits)
+    return _real_stats(np.ascontiguousarray(np.swapaxes(R_bits, 1, 2)).reshape(R_bits.shape), fn, rms_eps)
+
+
+def _stats_no_eps(R_bits, fn, rms_eps=1e-6):
+    return _real_stats(R_bits, fn, 0.0)
+
+
+def _split_no_post_mult(mixes, scale, base, hc=4, pre_eps=1e-6, post_mult=2.0):
+    return _real_split(mixes, scale, base, hc, pre_eps, 1.0)
+
+
+def _split_pre_without_eps(mixes, scale, base, hc=4, pre_eps=1e-6, post_mult=2.0):
+    return _real_split(mixes, scale, base, hc, 0.0, post_mult)
+
+
+def _combine_norm_no_eps(R_bits, pre, w_bits, eps=1e-6):
+    return _real_combine_norm(R_bits, pre, w_bits, 0.0)
+
+
+def _post_comb_transposed(x_bits, R_bits, post, comb):
+    return _real_post(x_bits, R_bits, post, np.swapaxes(np.asarray(comb), -1, -2))
+
+
+def _e4m3_truncating(s):
+    s = np.asarray(s, dtype=np.float64)
+    a = np.abs(s)
+    m, e = np.frexp(np.where(a > 0, a, 1.0))
+    p = e - 1
+    q = np.floor(np.ldexp(np.where(a > 0, a, 1.0), -(p - 3))).astype(np.int64)
+    code = np.where(a >= 2.0**-6, ((p + 7) << 3) | (q - 8), np.floor(np.ldexp(a, 9)).astype(np.int64))
+    code = np.where(a > 448, 0x7E, code) | np.where(np.signbit(s), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def _scale_exp_floor(amax):
+    amax = np.asarray(amax, dtype=np.float64)
+    pos = amax > 0
+    _, k = np.frexp(np.where(pos, amax, 1.0))
+    return np.clip(np.where(pos, k - 1 - 8, -127), -127, 127).astype(np.int64)
+
+
+def _run_all_pins():
+    """Run every pin; return the names of those that failed."""
+    failed = []
+    calls = [
+        ("sink_uniform", pins.test_sinkhorn_uniform_logits_fixed_point, ()),
+        ("sink_scaling", pins.test_sinkhorn_matches_scaling_vector_form_round_for_round, ()),
+        ("sink_cols", pins.test_sinkhorn_ends_on_columns, ()),
+        ("sink_eps", pins.test_sinkhorn_eps_is_added_to_entries, ()),
+        ("sink_perm", pins.test_sinkhorn_permutation_dominant, ()),
+        ("split_zero", pins.test_split_with_zero_scale_is_sigmoid_of_base, ()),
+        ("split_groups", pins.test_split_scales_go_to_their_groups, ()),
+        ("post_perm", pins.test_post_identity_and_permutation_are_exact, ()),
+        ("post_loops", pins.test_post_brute_force_loops, ()),
+        ("cn_onehot", pins.test_combine_norm_one_hot_pre_is_rms_norm, (3,)),
+        ("e4m3_torch", pins.test_e4m3_encode_matches_torch_cast_over_all_bf16_patterns, ()),
+        ("mx_minimal", pins.test_mxfp8_scale_exponent_is_minimal_and_safe, ()),
+    ]
+    for case in pins._golden_sinkhorn():
+        calls.append((f"sink_golden_{case[0]}", pins.test_sinkhorn_doubly_stochastic_rownorm_closed_form, (case,)))
+    for sh in [(1, 3), (2, 5)]:
+        calls.append((f"stats_onehot_{sh}", pins.test_stats_one_nonzero_closed_form, sh))
+    for case in pins._golden_mx():
+        calls.append((f"mx_hand_{case[2]!r}", pins.test_mxfp8_hand_cases, (case,)))
+    for name, fn, args in calls:
+        try:
+            fn(*args)
+        except AssertionError:
+            failed.append(name)
+    return failed
+
+
+MUTANTS = [
+    ("sinkhorn", _sinkhorn_row_last, "sink_"),
+    ("sinkhorn", _sinkhorn_one_round_short, "sink_scaling"),
+    ("sinkhorn", _sinkhorn_eps_only_in_denominators, "sink_eps"),
+    ("sinkhorn", _sinkhorn_transposed, "sink_"),
+    ("hc_mix_stats", _stats_h_major, "stats_onehot"),
+    ("hc_mix_stats", _stats_no_eps, "stats_onehot"),
+    ("hc_split", _split_no_post_mult, "split_"),
+    ("hc_split", _split_pre_without_eps, "split_"),
+    ("hc_combine_norm", _combine_norm_no_eps, "cn_onehot"),
+    ("hc_post", _post_comb_transposed, "post_"),
+    ("e4m3_encode", _e4m3_truncating, "e4m3_torch"),
+    ("mxfp8_scale_exponent", _scale_exp_floor, "mx_"),
+]
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert _run_all_pins() == []
+
+
+@pytest.mark.parametrize("attr,mutant,expect", MUTANTS, ids=[m[1].__name__ for m in MUTANTS])
+def test_planted_mistake_is_caught(monkeypatch, attr, mutant, expect):
+    monkeypatch.setattr(o, attr, mutant)
+    failed = _run_all_pins()
+    assert any(f.startswith(expect) for f in failed), failed

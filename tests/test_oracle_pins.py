@@ -1,0 +1,420 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself: closed forms,
+invariants, library routines (torch's bf16 / e4m3fn casts and rms_norm, scipy's expit),
+an independent scaling-vector Sinkhorn, arbitrary-precision brute force on tiny inputs and
+hand-derived format cases (tests/golden). No GPU is needed.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit
+
+from hyper_connection_residual_hc_amd import inputs
+from oracle import hc_oracle as o
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+EPS = 1e-6
+
+
+def _bf16_bits_of(values) -> np.ndarray:
+    """bf16 bit patterns of float values that are exact in bf16 (checked)."""
+    v = np.asarray(values, dtype=np.float64)
+    b = o.f64_to_bf16(v)
+    assert np.array_equal(o.bf16_to_f64(b), v, equal_nan=True) or np.all(
+        (o.bf16_to_f64(b) == v) | (np.isnan(v)))
+    return b
+
+
+# ------------------------------------------------------------------------------------------
+# bf16 conversions
+# ------------------------------------------------------------------------------------------
+def test_bf16_decode_all_patterns_matches_torch():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = o.bf16_to_f64(b)
+    ref = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref, equal_nan=True)
+
+
+def test_bf16_rounding_matches_torch_on_float32_inputs():
+    rng = np.random.default_rng(1)
+    u = rng.integers(0, 2**32, size=400_000, dtype=np.uint64).astype(np.uint32)
+    # add exact ties and near-ties around bf16 rounding points
+    base = rng.integers(0, 2**32, size=50_000, dtype=np.uint64).astype(np.uint32) & np.uint32(0xFFFF0000)
+    u = np.concatenate([u, base | np.uint32(0x8000), base | np.uint32(0x7FFF), base | np.uint32(0x8001),
+                        base | np.uint32(0x18000)])
+    f = u.view(np.float32)
+    f = f[np.isfinite(f)]
+    ours = o.f64_to_bf16(f.astype(np.float64))
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_rounding_is_single_rounding_from_float64():
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7 (ties to even -> 1); 2^-30 above it must round
+    # up. A value that went through float32 first would lose the 2^-30 and tie to even.
+    just_above = 1.0 + 2.0**-8 + 2.0**-30
+    assert o.bf16_to_f64(o.f64_to_bf16(just_above)) == 1.0 + 2.0**-7
+    assert o.bf16_to_f64(o.f64_to_bf16(1.0 + 2.0**-8)) == 1.0
+    assert o.bf16_to_f64(o.f64_to_bf16(-(1.0 + 3 * 2.0**-8))) == -(1.0 + 2 * 2.0**-7)
+    assert o.f64_to_bf16(-0.0) == 0x8000
+    assert o.f64_to_bf16(1e39) == 0x7F80
+    assert o.f64_to_bf16(float("nan")) == 0x7FC0
+
+
+# ------------------------------------------------------------------------------------------
+# stage 1: mix stats
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("stream,h", [(0, 0), (1, 3), (3, 7), (2, 5)])
+def test_stats_one_nonzero_closed_form(stream, h):
+    H = 8
+    fn = np.random.default_rng(2).standard_normal((24, 4 * H))
+    R = np.zeros((1, 4, H), dtype=np.uint16)
+    v = 3.25
+    R[0, stream, h] = _bf16_bits_of(v)
+    mixes, sumsq = o.hc_mix_stats(R, fn, EPS)
+    k = stream * H + h  # flatten(1) of [M, 4, H] is stream-major
+    want = v * fn[:, k] / math.sqrt(v * v / (4 * H) + EPS)
+    assert sumsq[0] == v * v
+    np.testing.assert_allclose(mixes[0], want, rtol=1e-14, atol=0)
+
+
+def test_stats_zero_row_gives_zero_mixes():
+    fn = np.random.default_rng(3).standard_normal((24, 4 * 16))
+    mixes, sumsq = o.hc_mix_stats(np.zeros((2, 4, 16), np.uint16), fn, EPS)
+    assert np.all(mixes == 0) and np.all(sumsq == 0)
+
+
+def test_stats_scale_invariance():
+    H = 64
+    fn, _, _ = inputs.hc_params(5, H=H)
+    R = inputs.residual(3, 7, H=H)
+    m1, _ = o.hc_mix_stats(inputs.bits(R), fn.numpy(), EPS)
+    m2, _ = o.hc_mix_stats(inputs.bits(R * 2), fn.numpy(), EPS)  # x2 is exact in bf16
+    np.testing.assert_allclose(m2, m1, rtol=2e-6, atol=1e-9)
+
+
+@pytest.mark.parametrize("H", [1, 2, 8])
+def test_stats_brute_force_mpmath(H):
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 50
+    rng = np.random.default_rng(H)
+    M = 3
+    R = _bf16_bits_of(np.round(rng.standard_normal((M, 4, H)) * 64) / 32)
+    fn = rng.standard_normal((24, 4 * H)).astype(np.float32)
+    mixes, _ = o.hc_mix_stats(R, fn, EPS)
+    xv = o.bf16_to_f64(R)
+    for m in range(M):
+        flat = [mpmath.mpf(float(xv[m, i, h])) for i in range(4) for h in range(H)]
+        ss = sum(t * t for t in flat)
+        r = 1 / mpmath.sqrt(ss / (4 * H) + mpmath.mpf(EPS))
+        for f in range(24):
+            d = sum(mpmath.mpf(float(fn[f, k])) * flat[k] for k in range(4 * H))
+            assert abs(float(d * r) - mixes[m, f]) <= 1e-13 * (1 + abs(float(d * r)))
+
+
+# ------------------------------------------------------------------------------------------
+# stage 2: split
+# ------------------------------------------------------------------------------------------
+def test_split_with_zero_scale_is_sigmoid_of_base():
+    _, _, base = inputs.hc_params(11, H=8)
+    base = base.numpy().astype(np.float64)
+    mixes = np.random.default_rng(4).standard_normal((5, 24)) * 10
+    pre, post, logits = o.hc_split(mixes, np.zeros(3), base)
+    np.testing.assert_allclose(pre, np.broadcast_to(expit(base[0:4]) + EPS, (5, 4)), rtol=1e-15)
+    np.testing.assert_allclose(post, np.broadcast_to(2 * expit(base[4:8]), (5, 4)), rtol=1e-15)
+    np.testing.assert_array_equal(logits, np.broadcast_to(base[8:].reshape(4, 4), (5, 4, 4)))
+
+
+def test_split_scales_go_to_their_groups():
+    mixes = np.zeros((1, 24))
+    mixes[0, 0], mixes[0, 4], mixes[0, 8] = 1.0, 1.0, 1.0
+    pre, post, logits = o.hc_split(mixes, np.array([2.0, 3.0, 5.0]), np.zeros(24))
+    assert pre[0, 0] == pytest.approx(expit(2.0) + EPS, rel=1e-15)
+    assert post[0, 0] == pytest.approx(2 * expit(3.0), rel=1e-15)
+    assert logits[0, 0, 0] == 5.0 and logits[0, 0, 1] == 0.0
+
+
+def test_pre_post_ranges_on_workload_inputs():
+    H = 256
+    fn, scale, base = inputs.hc_params(11, H=H)
+    R = inputs.residual(64, 64, H=H)
+    mixes, _ = o.hc_mix_stats(inputs.bits(R), fn.numpy(), EPS)
+    pre, post, comb = o.hc_split_sinkhorn(mixes, scale.numpy(), base.numpy())
+    assert np.all(pre >= EPS) and np.all(pre <= 1 + EPS)
+    assert np.all(post >= 0) and np.all(post <= 2)
+    assert np.all(comb > 0)
+
+
+# ------------------------------------------------------------------------------------------
+# stage 3: Sinkhorn
+# ------------------------------------------------------------------------------------------
+def test_sinkhorn_uniform_logits_fixed_point():
+    # every normalisation maps a uniform matrix with entry x to x / (4x + eps); the fixed
+    # point is (1 - eps) / 4, reached to rounding long before 20 rounds
+    P = o.sinkhorn(np.full((1, 4, 4), 0.7), 20, EPS)
+    np.testing.assert_allclose(P, (1 - EPS) / 4, rtol=1e-13)
+
+
+def _golden_sinkhorn():
+    rows = []
+    with open(os.path.join(GOLDEN, "sinkhorn_closed_forms.txt")) as fh:
+        for line in fh:
+            if not line.strip() or line.startswith("#"):
+                continue
+            parts = line.split()
+            vals = np.array([float(t) for t in parts[1:]])
+            rows.append((parts[0], vals[:16].reshape(4, 4), vals[16:].reshape(4, 4)))
+    return rows
+
+
+@pytest.mark.parametrize("case", _golden_sinkhorn(), ids=lambda c: c[0])
+def test_sinkhorn_doubly_stochastic_rownorm_closed_form(case):
+    _, A, want = case
+    L = np.log(A)[None] + 1.234  # softmax is shift invariant
+    np.testing.assert_allclose(o.sinkhorn(L, 20, 0.0)[0], want, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(o.sinkhorn(L, 20, EPS)[0], want, rtol=0, atol=5e-6)
+    # the transposed matrix gives the transposed answer: orientation matters
+    np.testing.assert_allclose(o.sinkhorn(np.log(A.T)[None], 20, 0.0)[0], want.T, atol=1e-13)
+
+
+def _scaling_vector_sinkhorn(L, rounds):
+    """Textbook Sinkhorn-Knopp on K = exp(L) with scaling vectors (eps = 0): round n sets
+    u = 1/(K v) (rows) then v = 1/(K^T u) (columns); the matrix is diag(u) K diag(v)."""
+    K = np.exp(L - L.max())
+    v = np.ones(K.shape[1])
+    for _ in range(rounds):
+        u = 1.0 / (K @ v)
+        v = 1.0 / (K.T @ u)
+    return u[:, None] * K * v[None, :]
+
+
+def test_sinkhorn_matches_scaling_vector_form_round_for_round():
+    rng = np.random.default_rng(6)
+    L = rng.standard_normal((8, 4, 4)) * 3
+    for rounds in (1, 2, 7, 20):
+        P = o.sinkhorn(L, rounds, 0.0)
+        for m in range(8):
+            np.testing.assert_allclose(P[m], _scaling_vector_sinkhorn(L[m], rounds), rtol=1e-12)
+    # 19 and 20 rounds are distinguishable on these inputs (the count is pinned)
+    assert np.max(np.abs(o.sinkhorn(L, 19, 0.0) - o.sinkhorn(L, 20, 0.0))) > 1e-7
+
+
+def test_sinkhorn_ends_on_columns():
+    # slowly converging logits (spread like base ~ 3 randn): after 20 rounds the columns sum
+    # to 1 within the eps effect, the rows not necessarily
+    rng = np.random.default_rng(7)
+    L = rng.standard_normal((4096, 4, 4)) * 3
+    P = o.sinkhorn(L, 20, EPS)
+    col = P.sum(axis=-2)
+    row = P.sum(axis=-1)
+    assert np.max(np.abs(col - 1)) < 5e-6
+    assert np.max(np.abs(row - 1)) > 1e-4  # so a row-last variant would fail the line above
+
+
+def test_sinkhorn_converges_to_doubly_stochastic():
+    rng = np.random.default_rng(8)
+    L = rng.standard_normal((64, 4, 4)) * 3
+    P0 = o.sinkhorn(L, 10000, 0.0)
+    assert np.max(np.abs(P0.sum(-1) - 1)) < 1e-10 and np.max(np.abs(P0.sum(-2) - 1)) < 1e-10
+    P = o.sinkhorn(L, 10000, EPS)
+    assert np.max(np.abs(P.sum(-1) - 1)) < 1e-5 and np.max(np.abs(P.sum(-2) - 1)) < 1e-5
+
+
+def test_sinkhorn_permutation_dominant():
+    perm = [2, 0, 3, 1]
+    Pm = np.zeros((4, 4))
+    Pm[np.arange(4), perm] = 1
+    P = o.sinkhorn((20 * Pm)[None], 20, EPS)[0]
+    np.testing.assert_allclose(P, Pm, atol=1e-5)
+
+
+def test_sinkhorn_eps_is_added_to_entries():
+    # an entry whose softmax weight is ~e^-60 ends near eps (eps is added after the
+    # softmax), not near e^-60
+    L = np.zeros((1, 4, 4))
+    L[0, 1, 2] = -60.0
+    P = o.sinkhorn(L, 20, EPS)
+    assert 0.5 * EPS < P[0, 1, 2] < 2 * EPS
+
+
+# ------------------------------------------------------------------------------------------
+# stage 4: combine + RMSNorm
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("i", [0, 3])
+def test_combine_norm_one_hot_pre_is_rms_norm(i):
+    H = 256
+    R = inputs.residual(4, 9, H=H)
+    w = inputs.norm_weight(12, H=H)
+    pre = np.zeros((4, 4))
+    pre[:, i] = 1.0
+    y, _ = o.hc_combine_norm(inputs.bits(R), pre, inputs.bits(w), EPS)
+    ref = torch.nn.functional.rms_norm(R[:, i, :].double(), (H,), w.double(), eps=EPS)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_combine_norm_zero_input_gives_zero():
+    y, yb = o.hc_combine_norm(np.zeros((2, 4, 32), np.uint16), np.full((2, 4), 0.3),
+                              inputs.bits(inputs.norm_weight(12, H=32)), EPS)
+    assert np.all(y == 0) and np.all(yb == 0)
+
+
+def test_combine_brute_force_loops():
+    H = 8
+    R = inputs.residual(2, 10, H=H)
+    pre = np.random.default_rng(11).random((2, 4))
+    c = o.hc_combine(inputs.bits(R), pre)
+    xv = o.bf16_to_f64(inputs.bits(R))
+    for m in range(2):
+        for h in range(H):
+            assert c[m, h] == pytest.approx(sum(pre[m, i] * xv[m, i, h] for i in range(4)), rel=1e-15)
+
+
+# ------------------------------------------------------------------------------------------
+# stage 5: hc post
+# ------------------------------------------------------------------------------------------
+def test_post_identity_and_permutation_are_exact():
+    H = 64
+    R = inputs.bits(inputs.residual(3, 12, H=H))
+    x = inputs.bits(inputs.sublayer_out(3, 13, H=H))
+    eye = np.broadcast_to(np.eye(4), (3, 4, 4))
+    _, out = o.hc_post(x, R, np.zeros((3, 4)), eye)
+    assert np.array_equal(out, R)
+    perm = [1, 3, 0, 2]  # destination j takes source perm[j]
+    P = np.zeros((4, 4))
+    P[perm, np.arange(4)] = 1  # comb[i, j] = 1 when i = perm[j]
+    _, out = o.hc_post(x, R, np.zeros((3, 4)), np.broadcast_to(P, (3, 4, 4)))
+    assert np.array_equal(out, R[:, perm, :])
+
+
+def test_post_only_post_term():
+    H = 64
+    R = inputs.bits(inputs.residual(2, 14, H=H))
+    x = inputs.bits(inputs.sublayer_out(2, 15, H=H))
+    post = np.zeros((2, 4))
+    post[:, 2] = 1.0
+    _, out = o.hc_post(x, R, post, np.zeros((2, 4, 4)))
+    assert np.array_equal(out[:, 2], x)
+    assert np.all(out[:, [0, 1, 3]] == 0)
+
+
+def test_post_brute_force_loops():
+    H = 4
+    R = inputs.bits(inputs.residual(2, 16, H=H))
+    x = inputs.bits(inputs.sublayer_out(2, 17, H=H))
+    rng = np.random.default_rng(18)
+    post, comb = rng.random((2, 4)) * 2, rng.random((2, 4, 4))
+    out, _ = o.hc_post(x, R, post, comb)
+    Rv, xv = o.bf16_to_f64(R), o.bf16_to_f64(x)
+    for m in range(2):
+        for j in range(4):
+            for h in range(H):
+                want = post[m, j] * xv[m, h] + sum(comb[m, i, j] * Rv[m, i, h] for i in range(4))
+                assert out[m, j, h] == pytest.approx(want, rel=1e-14, abs=1e-300)
+
+
+# ------------------------------------------------------------------------------------------
+# MXFP8
+# ------------------------------------------------------------------------------------------
+def _golden_mx():
+    cases = []
+    with open(os.path.join(GOLDEN, "mxfp8_hand_cases.txt")) as fh:
+        for line in fh:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            a, byte, v, code = line.split()
+            cases.append((float.fromhex(a), int(byte), float.fromhex(v), int(code, 16)))
+    return cases
+
+
+@pytest.mark.parametrize("case", _golden_mx(), ids=lambda c: f"{c[2]!r}")
+def test_mxfp8_hand_cases(case):
+    amax, byte, v, code = case
+    block = np.zeros(32)
+    block[0] = amax
+    block[1] = v
+    q, sf = o.mxfp8_quant_rows(_bf16_bits_of(block)[None, :])
+    assert int(sf[0, 0]) == byte
+    assert int(q[0, 1]) == code
+
+
+def test_e4m3_encode_matches_torch_cast_over_all_bf16_patterns():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = o.bf16_to_f64(b)
+    v = v[np.isfinite(v)]
+    for e in (-127, -20, -8, 0, 3, 8, 30, 120):
+        s = np.ldexp(v, -e)
+        keep = (np.abs(s) <= 448) & (np.abs(s) >= 2.0**-126)  # exact in float32, no saturation
+        s = s[keep]
+        ours = o.e4m3_encode(s)
+        ref = torch.from_numpy(s.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(ours, ref), e
+
+
+def test_e4m3_encode_is_nearest_even_by_brute_force():
+    codes = np.arange(256)
+    vals = o.e4m3_decode(codes)
+    finite = np.isfinite(vals)
+    rng = np.random.default_rng(19)
+    s = np.concatenate([rng.uniform(-448, 448, 3000), rng.uniform(-0.02, 0.02, 3000),
+                        vals[finite], (vals[finite][:-1] + vals[finite][1:]) / 2])
+    got = o.e4m3_encode(s)
+    for t, g in zip(s, got):
+        d = np.abs(vals[finite] - t)
+        best = np.flatnonzero(d == d.min())
+        cands = codes[finite][best]
+        if len(cands) > 1:  # tie: the even mantissa wins
+            cands = [c for c in cands if (c & 1) == 0 and (c & 0x7F) != 0] or \
+                    [c for c in cands if (c & 1) == 0]
+        assert o.e4m3_decode(g) == o.e4m3_decode(cands[0]) or (t == 0)
+
+
+def test_e4m3_saturates():
+    assert o.e4m3_encode(np.array([500.0, -1e6, 464.0]))[0] == 0x7E
+    assert list(o.e4m3_encode(np.array([500.0, -1e6, 464.0]))) == [0x7E, 0xFE, 0x7E]
+
+
+def test_mxfp8_scale_exponent_is_minimal_and_safe():
+    rng = np.random.default_rng(20)
+    amax = np.abs(o.bf16_to_f64(o.f64_to_bf16(np.exp(rng.uniform(-80, 80, 20000)))))
+    e = o.mxfp8_scale_exponent(amax)
+    assert np.all(np.ldexp(amax, -e) <= 448)
+    assert np.all(np.ldexp(amax, -(e - 1)) > 448)
+
+
+def test_mxfp8_dequant_error_bound_on_workload_rows():
+    y = inputs.mxfp8_rows(16, 21)
+    q, sf = o.mxfp8_quant_rows(inputs.bits(y))
+    v = o.bf16_to_f64(inputs.bits(y)).reshape(16, -1, 32)
+    e = sf.astype(np.int64) - 127
+    deq = np.ldexp(o.e4m3_decode(q).reshape(16, -1, 32), e[:, :, None])
+    amax = np.abs(v).max(-1, keepdims=True)
+    # e4m3 relative step is 2^-3 for normals; subnormal step 2^-9 in scaled units
+    err = np.abs(deq - v)
+    bound = np.maximum(np.abs(v) * 2.0**-4, np.ldexp(2.0**-10, e[:, :, None]))
+    assert np.all(err <= bound)
+    assert np.all(np.abs(deq) <= amax * (1 + 2.0**-3))
+
+
+def test_mxfp8_rejects_non_finite():
+    bad = _bf16_bits_of(np.zeros(32))[None, :].copy()
+    bad[0, 3] = 0x7F80
+    with pytest.raises(ValueError):
+        o.mxfp8_quant_rows(bad)
+
+
+# ------------------------------------------------------------------------------------------
+# hc_head
+# ------------------------------------------------------------------------------------------
+def test_hc_head_zero_scale_closed_form():
+    H = 16
+    R = inputs.residual(3, 22, H=H)
+    fn = np.random.default_rng(23).standard_normal((4, 4 * H))
+    base = np.array([0.3, -1.0, 2.0, 0.0])
+    y, _ = o.hc_head(inputs.bits(R), fn, np.array([0.0]), base)
+    pre = expit(base) + EPS
+    xv = o.bf16_to_f64(inputs.bits(R))
+    want = sum(pre[i] * xv[:, i, :] for i in range(4))
+    np.testing.assert_allclose(y, want, rtol=1e-14)
