@@ -1,0 +1,207 @@
+"""Throughput of the mHC post + pre hot path on one MI355X.
+
+One step = hc_post of the attention site followed by hc_pre of the FFN site on the same
+M = 4096 rows (H = 5120, 4 streams): the decoder layer's back-to-back sequence
+(deepseek_v4.py, DeepseekV4DecoderLayer.forward: hc_post(attn) then hc_pre(ffn)), i.e. one
+pre and one post over one batch. The post's coefficients come from an attention-site pre run
+at setup. Inputs are seeded synthetic tensors with the distributions of the one-GPU test page;
+several independent input sets rotate so that no step finds its inputs in the 256 MB
+Infinity Cache.
+
+Prints one JSON line: rows/s of the whole step, the HBM roofline of the dominant kernel
+(hc_post, timed live with HIP events on the stream it runs on) and the CPU oracle's rows/s
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+M_BENCH = 4096
+H = 5120
+HC = 4
+PEAK_HBM_GBS = 8000.0
+# algorithmic bytes per row (what the method must move at least once)
+POST_BYTES_ROW = 2 * (HC * H + H + HC * H) + 4 * (HC + HC * HC)  # R + x in, R' out, post + comb
+PRE_BYTES_ROW = 2 * (HC * H + H) + 4 * (HC + HC + HC * HC)  # R in, y out, pre/post/comb out
+PRE_BYTES_CALL = 24 * 4 * H * 4 + 2 * H  # fn (fp32 layout) and the norm weight, once per call
+STEP_BYTES = M_BENCH * (POST_BYTES_ROW + PRE_BYTES_ROW) + PRE_BYTES_CALL
+
+
+def cpu_baseline(rows: int, target_s: float):
+    """The oracle (as it stands) on `rows`-row samples of the same workload, repeated until
+    about target_s seconds of CPU work; returns rows/s and the BLAS thread count."""
+    import numpy as np
+
+    from hyper_connection_residual_hc_amd import inputs
+    from oracle import hc_oracle as o
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    fn_a, sc_a, ba_a = inputs.hc_params(inputs.SEED_ATTN)
+    fn_f, sc_f, ba_f = inputs.hc_params(inputs.SEED_FFN)
+    w_f = inputs.bits(inputs.norm_weight(inputs.SEED_NORM_FFN))
+    R = inputs.bits(inputs.residual(rows, M_BENCH))
+    x = inputs.bits(inputs.sublayer_out(rows, M_BENCH + 1))
+    pre_a = o.hc_pre(R, fn_a.numpy(), sc_a.numpy(), ba_a.numpy(),
+                     inputs.bits(inputs.norm_weight(inputs.SEED_NORM_ATTN)))
+    post32 = pre_a["post"].astype(np.float32)
+    comb32 = pre_a["comb"].astype(np.float32)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        _, R1 = o.hc_post(x, R, post32, comb32)
+        o.hc_pre(R1, fn_f.numpy(), sc_f.numpy(), ba_f.numpy(), w_f)
+        done += rows
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    return done / el, threads, el, done
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=3, help="rotating independent input sets")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the mHC path is row-local and this build has no "
+              "multi-GPU leg (rows would shard across GPUs with no exchange inside the path).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from hyper_connection_residual_hc_amd import _lib, inputs, ops
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from hyper_connection_residual_hc_amd import build
+        build.build()
+    dev = torch.device("cuda:0")
+    d = lambda t: t.to(dev).contiguous()  # noqa: E731
+
+    fn_a, sc_a, ba_a = map(d, inputs.hc_params(inputs.SEED_ATTN))
+    fn_f, sc_f, ba_f = map(d, inputs.hc_params(inputs.SEED_FFN))
+    w_a = d(inputs.norm_weight(inputs.SEED_NORM_ATTN))
+    w_f = d(inputs.norm_weight(inputs.SEED_NORM_FFN))
+    fnp_a, fnp_f = ops.fn_pack(fn_a), ops.fn_pack(fn_f)
+
+    M = M_BENCH
+    sets = []
+    for k in range(args.sets):
+        R = d(inputs.residual(M, M + 1000 * k))
+        x = d(inputs.sublayer_out(M, M + 1 + 1000 * k))
+        _, post, comb, _ = ops.pre(R, fnp_a, sc_a, ba_a, w_a)  # setup: attention-site pre
+        outs = dict(R1=torch.empty_like(R), y=torch.empty(M, H, dtype=torch.bfloat16, device=dev),
+                    post=torch.empty(M, HC, device=dev), comb=torch.empty(M, HC, HC, device=dev),
+                    ws=torch.empty(ops.pre_workspace_bytes(M, H), dtype=torch.uint8, device=dev))
+        sets.append((R, x, post, comb, outs))
+    torch.cuda.synchronize()
+
+    def step(k, ev=None):
+        R, x, post, comb, o = sets[k % len(sets)]
+        if ev is not None:
+            ev[0].record()
+        ops.post(x, R, post, comb, out=o["R1"])
+        if ev is not None:
+            ev[1].record()
+        ops.pre(o["R1"], fnp_f, sc_f, ba_f, w_f, out=(o["y"], o["post"], o["comb"], None),
+                workspace=o["ws"])
+        if ev is not None:
+            ev[2].record()
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    post_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    pre_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+
+    # practical HBM ceiling for context: a plain 1 GiB device copy
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    post_bytes = M * POST_BYTES_ROW
+    post_gbs = post_bytes / (post_ms * 1e-3) / 1e9
+    pre_bytes = M * PRE_BYTES_ROW + PRE_BYTES_CALL
+    rows_s = M / (ms_step * 1e-3)
+    step_gbs = STEP_BYTES / (ms_step * 1e-3) / 1e9
+    result = {
+        "metric": "mHC pre+post rows/s at M=4096, H=5120 (1 MI355X)",
+        "value": rows_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded, distributions of the one-GPU test page)",
+        "config": {
+            "workload": "mHC hc_post (attention site) then hc_pre (FFN site), M=4096 rows, "
+                        "H=5120, 4 streams, 20 Sinkhorn rounds, fused combine+RMSNorm",
+            "M": M, "H": H, "hc": HC, "io_dtype": "bf16", "input_sets": args.sets,
+            "parallelism": "none (1 GPU)",
+        },
+        "achieved_gbps_step": step_gbs,
+        "hbm_frac_step": step_gbs / PEAK_HBM_GBS,
+        "algorithmic_bytes_step": STEP_BYTES,
+        "copy_ceiling_gbps": copy_gbs,
+        "kernels_ms": {"hc_post": post_ms, "hc_pre (stats + finish)": pre_ms},
+        "pre_gbps": pre_bytes / (pre_ms * 1e-3) / 1e9,
+        "roofline": {
+            "kernel": "hc_post (post_kernel)",
+            "bound": "hbm",
+            "achieved": post_gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": post_gbs / PEAK_HBM_GBS,
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        v, cores, el, done = cpu_baseline(args.cpu_rows, args.cpu_seconds)
+        result["cpu_baseline"] = {
+            "value": v, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} rows ({args.cpu_rows}-row batches of the same post+pre workload, "
+                      f"{el:.1f} s, numpy float64)",
+        }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

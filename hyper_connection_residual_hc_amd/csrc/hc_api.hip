@@ -1,0 +1,260 @@
+// C ABI of the library (include/hc_mi355x.h): argument validation, then the kernel launches.
+// No entry point allocates, frees or synchronises; every check happens before anything is
+// enqueued, so an error return leaves the stream untouched.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/hc_mi355x.h"
+#include "hc_launch.h"
+
+namespace {
+
+using hc::kHC;
+using hc::kMix;
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// [begin, end) byte ranges of strided row tensors, for overlap checks
+struct Span {
+  uintptr_t b, e;
+};
+Span rows_span(const void* p, int64_t M, int64_t ld, int64_t row_elems, int64_t elem_bytes) {
+  const uintptr_t b = (uintptr_t)p;
+  return {b, b + (uintptr_t)(((M - 1) * ld + row_elems) * elem_bytes)};
+}
+bool overlaps(Span a, Span b) { return a.b < b.e && b.b < a.e; }
+
+bool finite_nonneg(float v) { return isfinite(v) && v >= 0.0f; }
+
+int check_m(int64_t M) {
+  if (M < 0 || M >= kMaxRows) return HC_ERR_ARG;
+  return HC_OK;
+}
+
+int launched(hipError_t err) { return err == hipSuccess ? HC_OK : HC_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool stats_h_ok(int32_t H) { return H > 0 && H % 256 == 0 && H <= (1 << 20); }
+bool post_h_ok(int32_t H) { return H > 0 && H % 512 == 0 && H <= (1 << 20); }
+
+// R [M, 4, H] bf16 with row stride ldR
+int check_residual(const uint16_t* R, int64_t ldR, int32_t H) {
+  if (ldR < (int64_t)kHC * H) return HC_ERR_SHAPE;
+  if (!al16(R) || (ldR * 2) % 16) return HC_ERR_ALIGN;
+  return HC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+HC_API const char* hc_status_string(int status) {
+  switch (status) {
+    case HC_OK: return "HC_OK";
+    case HC_ERR_NULL: return "HC_ERR_NULL";
+    case HC_ERR_SHAPE: return "HC_ERR_SHAPE";
+    case HC_ERR_ALIGN: return "HC_ERR_ALIGN";
+    case HC_ERR_ALIAS: return "HC_ERR_ALIAS";
+    case HC_ERR_WORKSPACE: return "HC_ERR_WORKSPACE";
+    case HC_ERR_LAUNCH: return "HC_ERR_LAUNCH";
+    case HC_ERR_ARG: return "HC_ERR_ARG";
+    default: return "HC_ERR_UNKNOWN";
+  }
+}
+
+HC_API int hc_abi_version(void) { return 100; }
+
+// ---- fn packing --------------------------------------------------------------------------
+HC_API size_t hc_fn_packed_bytes(int32_t H) {
+  if (!stats_h_ok(H)) return 0;
+  return (size_t)hc::packed_fn_elems(H) * 2;
+}
+
+HC_API int hc_fn_pack(const float* fn, int32_t H, uint16_t* fn_packed, void* stream) {
+  if (!stats_h_ok(H)) return HC_ERR_SHAPE;
+  if (!fn || !fn_packed) return HC_ERR_NULL;
+  if (!al16(fn_packed)) return HC_ERR_ALIGN;
+  const Span in{(uintptr_t)fn, (uintptr_t)fn + (uintptr_t)kMix * 4 * H * 4};
+  const Span out{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)};
+  if (overlaps(in, out)) return HC_ERR_ALIAS;
+  return launched(hc::launch_fn_pack(fn, H, fn_packed, as_stream(stream)));
+}
+
+// ---- stage 1 -----------------------------------------------------------------------------
+HC_API size_t hc_pre_stats_workspace_bytes(int64_t M, int32_t H) {
+  if (M < 0 || !stats_h_ok(H)) return 0;
+  return hc::stats_workspace_bytes(M);
+}
+
+HC_API int hc_pre_stats(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, int64_t M,
+                        int32_t H, float rms_eps, float* mixes, float* sumsq, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if (!stats_h_ok(H)) return HC_ERR_SHAPE;
+  if (!finite_nonneg(rms_eps)) return HC_ERR_ARG;
+  if (M == 0) return HC_OK;
+  if (!R || !fn_packed || !mixes) return HC_ERR_NULL;
+  if ((st = check_residual(R, ldR, H))) return st;
+  if (!al16(fn_packed)) return HC_ERR_ALIGN;
+  if (!workspace || workspace_bytes < hc::stats_workspace_bytes(M)) return HC_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return HC_ERR_ALIGN;
+  const Span r = rows_span(R, M, ldR, (int64_t)kHC * H, 2);
+  const Span fp{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)};
+  const Span mx = rows_span(mixes, M, kMix, kMix, 4);
+  const Span ws{(uintptr_t)workspace, (uintptr_t)workspace + hc::stats_workspace_bytes(M)};
+  if (overlaps(mx, r) || overlaps(mx, fp) || overlaps(ws, r) || overlaps(ws, fp) ||
+      overlaps(ws, mx))
+    return HC_ERR_ALIAS;
+  if (sumsq) {
+    const Span sq = rows_span(sumsq, M, 1, 1, 4);
+    if (overlaps(sq, r) || overlaps(sq, fp) || overlaps(sq, mx) || overlaps(sq, ws))
+      return HC_ERR_ALIAS;
+  }
+  float* part = static_cast<float*>(workspace);
+  hipStream_t s = as_stream(stream);
+  if ((st = launched(hc::launch_stats(R, ldR, fn_packed, (int)M, H, part, s)))) return st;
+  return launched(hc::launch_stats_reduce(part, (int)M, H, rms_eps, mixes, sumsq, s));
+}
+
+// ---- stages 2-3 ----------------------------------------------------------------------------
+HC_API int hc_sinkhorn(const float* mixes, int64_t M, const float* scale, const float* base,
+                       int32_t iters, float pre_eps, float sinkhorn_eps, float post_mult,
+                       float* pre, float* post, float* comb, void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if (iters < 1 || iters > 100000) return HC_ERR_SHAPE;
+  if (!finite_nonneg(pre_eps) || !finite_nonneg(sinkhorn_eps) || !isfinite(post_mult))
+    return HC_ERR_ARG;
+  if (M == 0) return HC_OK;
+  if (!mixes || !scale || !base || !pre || !post || !comb) return HC_ERR_NULL;
+  const Span in = rows_span(mixes, M, kMix, kMix, 4);
+  const Span sc{(uintptr_t)scale, (uintptr_t)scale + 12};
+  const Span bs{(uintptr_t)base, (uintptr_t)base + kMix * 4};
+  const Span outs[3] = {rows_span(pre, M, kHC, kHC, 4), rows_span(post, M, kHC, kHC, 4),
+                        rows_span(comb, M, kHC * kHC, kHC * kHC, 4)};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], in) || overlaps(outs[i], sc) || overlaps(outs[i], bs)) return HC_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outs[j])) return HC_ERR_ALIAS;
+  }
+  return launched(hc::launch_sinkhorn(mixes, (int)M, scale, base, iters, pre_eps, sinkhorn_eps,
+                                      post_mult, pre, post, comb, as_stream(stream)));
+}
+
+// ---- stage 4 -------------------------------------------------------------------------------
+HC_API int hc_combine_norm(const uint16_t* R, int64_t ldR, const float* pre, int64_t ldPre,
+                           const uint16_t* weight, int64_t M, int32_t H, float eps, uint16_t* y,
+                           int64_t ldY, void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if (!hc::combine_h_supported(H)) return HC_ERR_SHAPE;
+  if (!finite_nonneg(eps)) return HC_ERR_ARG;
+  if (M == 0) return HC_OK;
+  if (!R || !pre || !weight || !y) return HC_ERR_NULL;
+  if ((st = check_residual(R, ldR, H))) return st;
+  if (ldPre < kHC || ldY < H) return HC_ERR_SHAPE;
+  if (!al16(weight) || !al16(y) || (ldY * 2) % 16) return HC_ERR_ALIGN;
+  const Span out = rows_span(y, M, ldY, H, 2);
+  if (overlaps(out, rows_span(R, M, ldR, (int64_t)kHC * H, 2)) ||
+      overlaps(out, rows_span(pre, M, ldPre, kHC, 4)) ||
+      overlaps(out, Span{(uintptr_t)weight, (uintptr_t)weight + (uintptr_t)H * 2}))
+    return HC_ERR_ALIAS;
+  return launched(hc::launch_combine_norm(R, ldR, pre, ldPre, weight, (int)M, H, eps, y, ldY,
+                                          as_stream(stream)));
+}
+
+// ---- stage 5 -------------------------------------------------------------------------------
+HC_API int hc_post(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                   const float* post, const float* comb, int64_t M, int32_t H, uint16_t* Rout,
+                   int64_t ldOut, void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if (!post_h_ok(H)) return HC_ERR_SHAPE;
+  if (M * (H / 512) >= kMaxRows) return HC_ERR_ARG;
+  if (M == 0) return HC_OK;
+  if (!x || !R || !post || !comb || !Rout) return HC_ERR_NULL;
+  if ((st = check_residual(R, ldR, H))) return st;
+  if (ldX < H || ldOut < (int64_t)kHC * H) return HC_ERR_SHAPE;
+  if (!al16(x) || !al16(Rout) || (ldX * 2) % 16 || (ldOut * 2) % 16) return HC_ERR_ALIGN;
+  const Span out = rows_span(Rout, M, ldOut, (int64_t)kHC * H, 2);
+  if (overlaps(out, rows_span(x, M, ldX, H, 2)) ||
+      overlaps(out, rows_span(R, M, ldR, (int64_t)kHC * H, 2)) ||
+      overlaps(out, rows_span(post, M, kHC, kHC, 4)) ||
+      overlaps(out, rows_span(comb, M, kHC * kHC, kHC * kHC, 4)))
+    return HC_ERR_ALIAS;
+  return launched(hc::launch_post(x, ldX, R, ldR, post, comb, (int)M, H, Rout, ldOut,
+                                  as_stream(stream)));
+}
+
+// ---- MXFP8 -----------------------------------------------------------------------------------
+HC_API int mxfp8_quant_rows(const uint16_t* y, int64_t ldY, int64_t M, int32_t K, uint8_t* q,
+                            int64_t ldQ, uint8_t* scales, int64_t ldS, void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if (K <= 0 || K % 32 || K > (1 << 24)) return HC_ERR_SHAPE;
+  if (M * (K / 32) >= kMaxRows * 16) return HC_ERR_ARG;
+  if (M == 0) return HC_OK;
+  if (!y || !q || !scales) return HC_ERR_NULL;
+  if (ldY < K || ldQ < K || ldS < K / 32) return HC_ERR_SHAPE;
+  if (!al16(y) || !al16(q) || (ldY * 2) % 16 || ldQ % 16) return HC_ERR_ALIGN;
+  const Span in = rows_span(y, M, ldY, K, 2);
+  const Span qs = rows_span(q, M, ldQ, K, 1);
+  const Span ss = rows_span(scales, M, ldS, K / 32, 1);
+  if (overlaps(qs, in) || overlaps(ss, in) || overlaps(qs, ss)) return HC_ERR_ALIAS;
+  return launched(hc::launch_mxfp8(y, ldY, (int)M, K, q, ldQ, scales, ldS, as_stream(stream)));
+}
+
+// ---- fused pre -------------------------------------------------------------------------------
+HC_API size_t hc_pre_workspace_bytes(int64_t M, int32_t H) {
+  return hc_pre_stats_workspace_bytes(M, H);
+}
+
+HC_API int hc_pre(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, const float* scale,
+                  const float* base, const uint16_t* weight, int64_t M, int32_t H,
+                  float rms_eps, float pre_eps, float sinkhorn_eps, int32_t iters,
+                  float post_mult, float norm_eps, uint16_t* y, int64_t ldY, float* pre,
+                  float* post, float* comb, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if (!stats_h_ok(H) || !hc::combine_h_supported(H)) return HC_ERR_SHAPE;
+  if (iters < 1 || iters > 100000) return HC_ERR_SHAPE;
+  if (!finite_nonneg(rms_eps) || !finite_nonneg(pre_eps) || !finite_nonneg(sinkhorn_eps) ||
+      !finite_nonneg(norm_eps) || !isfinite(post_mult))
+    return HC_ERR_ARG;
+  if (M == 0) return HC_OK;
+  if (!R || !fn_packed || !scale || !base || !weight || !y || !post || !comb) return HC_ERR_NULL;
+  if ((st = check_residual(R, ldR, H))) return st;
+  if (ldY < H) return HC_ERR_SHAPE;
+  if (!al16(fn_packed) || !al16(weight) || !al16(y) || (ldY * 2) % 16) return HC_ERR_ALIGN;
+  if (!workspace || workspace_bytes < hc::stats_workspace_bytes(M)) return HC_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return HC_ERR_ALIGN;
+  const Span ins[5] = {rows_span(R, M, ldR, (int64_t)kHC * H, 2),
+                       Span{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)},
+                       Span{(uintptr_t)scale, (uintptr_t)scale + 12},
+                       Span{(uintptr_t)base, (uintptr_t)base + kMix * 4},
+                       Span{(uintptr_t)weight, (uintptr_t)weight + (uintptr_t)H * 2}};
+  Span outs[5] = {rows_span(y, M, ldY, H, 2), rows_span(post, M, kHC, kHC, 4),
+                  rows_span(comb, M, kHC * kHC, kHC * kHC, 4),
+                  Span{(uintptr_t)workspace, (uintptr_t)workspace + hc::stats_workspace_bytes(M)},
+                  pre ? rows_span(pre, M, kHC, kHC, 4) : Span{0, 0}};
+  for (int i = 0; i < 5; ++i) {
+    if (outs[i].b == outs[i].e) continue;
+    for (int j = 0; j < 5; ++j)
+      if (overlaps(outs[i], ins[j])) return HC_ERR_ALIAS;
+    for (int j = i + 1; j < 5; ++j)
+      if (outs[j].b != outs[j].e && overlaps(outs[i], outs[j])) return HC_ERR_ALIAS;
+  }
+  float* part = static_cast<float*>(workspace);
+  hipStream_t s = as_stream(stream);
+  if ((st = launched(hc::launch_stats(R, ldR, fn_packed, (int)M, H, part, s)))) return st;
+  return launched(hc::launch_pre_finish(part, R, ldR, scale, base, weight, (int)M, H, rms_eps,
+                                        pre_eps, sinkhorn_eps, iters, post_mult, norm_eps, y, ldY,
+                                        pre, post, comb, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,200 @@
+// Stages 2-4 of hc pre (deepseek_v4.py, DeepseekV4DecoderLayer.hc_pre):
+//   split + Sinkhorn of the 24 mixes into pre(4), post(4), comb(4x4), then
+//   y = bf16( c * rsqrt(mean(c^2) + eps) * w ),  c = sum_i pre_i * R_i   (one rounding).
+//
+// Work layout: one wavefront per row. The row's split + Sinkhorn runs on a 16-lane group
+// (one lane per comb entry, row sums over the lane quad, column sums over lanes e^4, e^8);
+// the wave's four 16-lane groups compute the same row, so every lane ends up holding the row's
+// values without LDS or a barrier. The combine then streams the row: each lane owns 8 columns
+// of every 512-column block of all four streams (16-byte accesses, wave-wide 1 KB), keeps c in
+// registers, reduces sum(c^2) across the wave in a fixed butterfly order and writes y.
+#include "hc_launch.h"
+
+namespace hc {
+
+// ---- split + Sinkhorn, standalone -----------------------------------------------------------
+__global__ __launch_bounds__(256) void sinkhorn_kernel(const float* __restrict__ mixes, int M,
+                                                       const float* __restrict__ scale,
+                                                       const float* __restrict__ base, int iters,
+                                                       float pre_eps, float sk_eps,
+                                                       float post_mult, float* __restrict__ pre,
+                                                       float* __restrict__ post,
+                                                       float* __restrict__ comb) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int m = (int)(gid >> 4);
+  const int e = (int)(gid & 15);
+  // every lane of a 16-lane group takes part in the cross-lane sums: rows past the end
+  // recompute the last row and store nothing
+  const bool valid = m < M;
+  const int mm = valid ? m : M - 1;
+  const SplitParams sp{scale[0], scale[1], scale[2], iters, pre_eps, sk_eps, post_mult};
+  const float* mx = mixes + (int64_t)mm * kMix;
+  const float mix_a = e < 8 ? mx[e] : 0.0f;
+  const float base_a = e < 8 ? base[e] : 0.0f;
+  float pp;
+  const float c = split_sinkhorn_lane(e, mix_a, mx[8 + e], base_a, base[8 + e], sp, &pp);
+  if (!valid) return;
+  comb[(int64_t)mm * 16 + e] = c;
+  if (e < 4) {
+    pre[(int64_t)mm * kHC + e] = pp;
+  } else if (e < 8) {
+    post[(int64_t)mm * kHC + (e - 4)] = pp;
+  }
+}
+
+hipError_t launch_sinkhorn(const float* mixes, int M, const float* scale, const float* base,
+                           int iters, float pre_eps, float sk_eps, float post_mult, float* pre,
+                           float* post, float* comb, hipStream_t s) {
+  const int64_t threads = (int64_t)M * 16;
+  hipLaunchKernelGGL(sinkhorn_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     mixes, M, scale, base, iters, pre_eps, sk_eps, post_mult, pre, post, comb);
+  return hipGetLastError();
+}
+
+// ---- combine + RMSNorm of one row by one wavefront ------------------------------------------
+// NG = H / 512 column blocks; lane covers columns [512 g + 8 lane, +8) of each block g.
+template <int NG>
+__device__ __forceinline__ void combine_norm_row(const uint16_t* __restrict__ Rr,
+                                                 const float (&p)[kHC],
+                                                 const uint16_t* __restrict__ w, float eps,
+                                                 uint16_t* __restrict__ yr, int lane) {
+  constexpr int H = NG * 512;
+  u32x4 rv[NG][kHC];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < kHC; ++i) rv[g][i] = ld16_stream(Rr + i * H + g * 512 + lane * 8);
+
+  float c[NG][8];
+  float ss = 0.0f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float r[kHC][8];
+#pragma unroll
+    for (int i = 0; i < kHC; ++i) unpack8(rv[g][i], r[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = p[0] * r[0][e];
+#pragma unroll
+      for (int i = 1; i < kHC; ++i) a = __fmaf_rn(p[i], r[i][e], a);
+      c[g][e] = a;
+      ss = __fmaf_rn(a, a, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  const float rn = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float wf[8], o[8];
+    unpack8(ld16(w + g * 512 + lane * 8), wf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (c[g][e] * rn) * wf[e];
+    st16(yr + g * 512 + lane * 8, pack8(o));
+  }
+}
+
+template <int NG>
+__global__ __launch_bounds__(256) void combine_norm_kernel(const uint16_t* __restrict__ R,
+                                                           int64_t ldR,
+                                                           const float* __restrict__ pre,
+                                                           int64_t ldPre,
+                                                           const uint16_t* __restrict__ w, int M,
+                                                           float eps, uint16_t* __restrict__ y,
+                                                           int64_t ldY) {
+  const int lane = threadIdx.x & 63;
+  const int m = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
+  if (m >= M) return;
+  float p[kHC];
+#pragma unroll
+  for (int i = 0; i < kHC; ++i) p[i] = pre[(int64_t)m * ldPre + i];
+  combine_norm_row<NG>(R + (int64_t)m * ldR, p, w, eps, y + (int64_t)m * ldY, lane);
+}
+
+// ---- fused: slice reduce + split + Sinkhorn + combine + RMSNorm ----------------------------
+template <int NG>
+__global__ __launch_bounds__(256) void pre_finish_kernel(
+    const float* __restrict__ part, const uint16_t* __restrict__ R, int64_t ldR,
+    const float* __restrict__ scale, const float* __restrict__ base,
+    const uint16_t* __restrict__ w, int M, float kf, float rms_eps, float pre_eps, float sk_eps,
+    int iters, float post_mult, float norm_eps, uint16_t* __restrict__ y, int64_t ldY,
+    float* __restrict__ pre, float* __restrict__ post, float* __restrict__ comb) {
+  const int lane = threadIdx.x & 63;
+  const int m = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
+  if (m >= M) return;  // wave-uniform: the whole wave leaves together
+  const int e = lane & 15;
+
+  // mixes for this lane's entries, reduced over the slices exactly as stats_reduce does
+  const float ss = slice_sum(part, M, m, kMix);
+  const float rs = mix_rscale(ss, kf, rms_eps);
+  const float mix_a = e < 8 ? slice_sum(part, M, m, e) * rs : 0.0f;
+  const float mix_c = slice_sum(part, M, m, 8 + e) * rs;
+  const SplitParams sp{scale[0], scale[1], scale[2], iters, pre_eps, sk_eps, post_mult};
+  const float base_a = e < 8 ? base[e] : 0.0f;
+  float pp;
+  const float cv = split_sinkhorn_lane(e, mix_a, mix_c, base_a, base[8 + e], sp, &pp);
+  if (lane < 16) {
+    comb[(int64_t)m * 16 + e] = cv;
+    if (e < 4) {
+      if (pre) pre[(int64_t)m * kHC + e] = pp;
+    } else if (e < 8) {
+      post[(int64_t)m * kHC + (e - 4)] = pp;
+    }
+  }
+  float p[kHC];
+#pragma unroll
+  for (int i = 0; i < kHC; ++i) p[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), i));
+  combine_norm_row<NG>(R + (int64_t)m * ldR, p, w, norm_eps, y + (int64_t)m * ldY, lane);
+}
+
+// ---- dispatch over the compiled H values ----------------------------------------------------
+#define HC_FOR_EACH_NG(X) X(1) X(2) X(4) X(8) X(10) X(14) X(16)
+
+bool combine_h_supported(int H) {
+  if (H % 512) return false;
+  switch (H / 512) {
+#define HC_CASE(n) case n: return true;
+    HC_FOR_EACH_NG(HC_CASE)
+#undef HC_CASE
+    default: return false;
+  }
+}
+
+hipError_t launch_combine_norm(const uint16_t* R, int64_t ldR, const float* pre, int64_t ldPre,
+                               const uint16_t* w, int M, int H, float eps, uint16_t* y,
+                               int64_t ldY, hipStream_t s) {
+  const dim3 grid((unsigned)((M + 3) / 4)), block(256);
+  switch (H / 512) {
+#define HC_CASE(n)                                                                              \
+  case n:                                                                                       \
+    hipLaunchKernelGGL(combine_norm_kernel<n>, grid, block, 0, s, R, ldR, pre, ldPre, w, M,     \
+                       eps, y, ldY);                                                            \
+    break;
+    HC_FOR_EACH_NG(HC_CASE)
+#undef HC_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pre_finish(const float* part, const uint16_t* R, int64_t ldR,
+                             const float* scale, const float* base, const uint16_t* w, int M,
+                             int H, float rms_eps, float pre_eps, float sk_eps, int iters,
+                             float post_mult, float norm_eps, uint16_t* y, int64_t ldY,
+                             float* pre, float* post, float* comb, hipStream_t s) {
+  const dim3 grid((unsigned)((M + 3) / 4)), block(256);
+  const float kf = (float)(4 * H);
+  switch (H / 512) {
+#define HC_CASE(n)                                                                              \
+  case n:                                                                                       \
+    hipLaunchKernelGGL(pre_finish_kernel<n>, grid, block, 0, s, part, R, ldR, scale, base, w,   \
+                       M, kf, rms_eps, pre_eps, sk_eps, iters, post_mult, norm_eps, y, ldY,    \
+                       pre, post, comb);                                                        \
+    break;
+    HC_FOR_EACH_NG(HC_CASE)
+#undef HC_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hc

@@ -1,0 +1,221 @@
+"""Python binding of the mHC pre/post library: argument marshalling only.
+
+Every function takes and returns torch tensors on a ROCm device, passes their device
+pointers and row strides to the C ABI (include/hc_mi355x.h) and enqueues on torch's current
+stream. All arithmetic happens in the HIP kernels. Output tensors are allocated with torch
+when the caller does not pass them.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+HC = 4
+MIX = 24
+RMS_EPS = 1e-6
+HC_EPS = 1e-6
+ITERS = 20
+POST_MULT = 2.0
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if t.numel() and t.stride(-1) != 1:
+        raise ValueError(f"{name} needs a unit inner stride")
+
+
+def _residual(R: torch.Tensor):
+    _need(R, "R", torch.bfloat16, 3)
+    M, hc, H = R.shape
+    if hc != HC:
+        raise ValueError(f"R must be [M, {HC}, H], got {tuple(R.shape)}")
+    if M and R.stride(1) != H:
+        raise ValueError("R's streams must be contiguous inside a row")
+    return M, H, (R.stride(0) if M else HC * H)
+
+
+def _rows(t: torch.Tensor, width: int) -> int:
+    return t.stride(0) if t.shape[0] else width
+
+
+def _contig(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None:
+    _need(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {tuple(shape)} tensor, got {tuple(t.shape)}")
+
+
+# ---- weight preparation -------------------------------------------------------------------
+def fn_packed_bytes(H: int) -> int:
+    return int(_lib.lib().hc_fn_packed_bytes(H))
+
+
+def fn_pack(fn: torch.Tensor) -> torch.Tensor:
+    """fp32 fn [24, 4H] -> the packed bf16 hi/mid/lo form hc_pre_stats and hc_pre read."""
+    _need(fn, "fn", torch.float32, 2)
+    if fn.shape[0] != MIX or fn.shape[1] % HC or not fn.is_contiguous():
+        raise ValueError(f"fn must be a contiguous [{MIX}, 4H] tensor, got {tuple(fn.shape)}")
+    H = fn.shape[1] // HC
+    nbytes = fn_packed_bytes(H)
+    if nbytes == 0:
+        raise ValueError(f"unsupported H={H}")
+    out = torch.empty(nbytes // 2, dtype=torch.int16, device=fn.device)
+    _lib.call("hc_fn_pack", fn.data_ptr(), H, out.data_ptr(), _stream(fn))
+    return out
+
+
+# ---- stage 1 ---------------------------------------------------------------------------------
+def stats_workspace_bytes(M: int, H: int) -> int:
+    return int(_lib.lib().hc_pre_stats_workspace_bytes(M, H))
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if workspace is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def pre_stats(R: torch.Tensor, fn_packed: torch.Tensor, rms_eps: float = RMS_EPS,
+              mixes: Optional[torch.Tensor] = None, sumsq: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, want_sumsq: bool = True):
+    """(mixes fp32 [M, 24], sumsq fp32 [M] or None)."""
+    M, H, ldR = _residual(R)
+    if mixes is None:
+        mixes = torch.empty(M, MIX, dtype=torch.float32, device=R.device)
+    _contig(mixes, "mixes", torch.float32, (M, MIX))
+    if sumsq is None and want_sumsq:
+        sumsq = torch.empty(M, dtype=torch.float32, device=R.device)
+    if sumsq is not None:
+        _contig(sumsq, "sumsq", torch.float32, (M,))
+    ws = _workspace(stats_workspace_bytes(M, H), R.device, workspace)
+    _lib.call("hc_pre_stats", R.data_ptr(), ldR, fn_packed.data_ptr(), M, H, rms_eps,
+              mixes.data_ptr(), _ptr(sumsq), ws.data_ptr(), ws.numel() * ws.element_size(),
+              _stream(R))
+    return mixes, sumsq
+
+
+# ---- stages 2-3 ------------------------------------------------------------------------------
+def sinkhorn(mixes: torch.Tensor, scale: torch.Tensor, base: torch.Tensor, iters: int = ITERS,
+             pre_eps: float = HC_EPS, sinkhorn_eps: float = HC_EPS, post_mult: float = POST_MULT,
+             out=None):
+    """(pre [M, 4], post [M, 4], comb [M, 4, 4]) fp32."""
+    M = mixes.shape[0]
+    _contig(mixes, "mixes", torch.float32, (M, MIX))
+    _contig(scale, "scale", torch.float32, (3,))
+    _contig(base, "base", torch.float32, (MIX,))
+    if out is None:
+        out = (torch.empty(M, HC, dtype=torch.float32, device=mixes.device),
+               torch.empty(M, HC, dtype=torch.float32, device=mixes.device),
+               torch.empty(M, HC, HC, dtype=torch.float32, device=mixes.device))
+    pre, post, comb = out
+    _contig(pre, "pre", torch.float32, (M, HC))
+    _contig(post, "post", torch.float32, (M, HC))
+    _contig(comb, "comb", torch.float32, (M, HC, HC))
+    _lib.call("hc_sinkhorn", mixes.data_ptr(), M, scale.data_ptr(), base.data_ptr(), iters,
+              pre_eps, sinkhorn_eps, post_mult, pre.data_ptr(), post.data_ptr(), comb.data_ptr(),
+              _stream(mixes))
+    return pre, post, comb
+
+
+# ---- stage 4 ---------------------------------------------------------------------------------
+def combine_norm(R: torch.Tensor, pre: torch.Tensor, weight: torch.Tensor,
+                 eps: float = RMS_EPS, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y bf16 [M, H] = RMSNorm(sum_i pre_i R_i) * weight."""
+    M, H, ldR = _residual(R)
+    _need(pre, "pre", torch.float32, 2)
+    if tuple(pre.shape) != (M, HC):
+        raise ValueError(f"pre must be [{M}, {HC}]")
+    _contig(weight, "weight", torch.bfloat16, (H,))
+    if out is None:
+        out = torch.empty(M, H, dtype=torch.bfloat16, device=R.device)
+    _need(out, "out", torch.bfloat16, 2)
+    _lib.call("hc_combine_norm", R.data_ptr(), ldR, pre.data_ptr(), _rows(pre, HC),
+              weight.data_ptr(), M, H, eps, out.data_ptr(), _rows(out, H), _stream(R))
+    return out
+
+
+# ---- stage 5 ---------------------------------------------------------------------------------
+def post(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.Tensor,
+         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """R' bf16 [M, 4, H] = post * x + comb^T R (per row)."""
+    M, H, ldR = _residual(R)
+    _need(x, "x", torch.bfloat16, 2)
+    if tuple(x.shape) != (M, H):
+        raise ValueError(f"x must be [{M}, {H}]")
+    _contig(post_, "post", torch.float32, (M, HC))
+    _contig(comb, "comb", torch.float32, (M, HC, HC))
+    if out is None:
+        out = torch.empty(M, HC, H, dtype=torch.bfloat16, device=R.device)
+    _residual(out)
+    _lib.call("hc_post", x.data_ptr(), _rows(x, H), R.data_ptr(), ldR, post_.data_ptr(),
+              comb.data_ptr(), M, H, out.data_ptr(), _rows(out, HC * H), _stream(R))
+    return out
+
+
+# ---- MXFP8 -----------------------------------------------------------------------------------
+def mxfp8_quant_rows(y: torch.Tensor, q: Optional[torch.Tensor] = None,
+                     scales: Optional[torch.Tensor] = None):
+    """(q uint8 [M, K] e4m3fn codes, scales uint8 [M, K/32] ue8m0, linear)."""
+    _need(y, "y", torch.bfloat16, 2)
+    M, K = y.shape
+    if q is None:
+        q = torch.empty(M, K, dtype=torch.uint8, device=y.device)
+    if scales is None:
+        scales = torch.empty(M, K // 32, dtype=torch.uint8, device=y.device)
+    _need(q, "q", torch.uint8, 2)
+    _need(scales, "scales", torch.uint8, 2)
+    _lib.call("mxfp8_quant_rows", y.data_ptr(), _rows(y, K), M, K, q.data_ptr(), _rows(q, K),
+              scales.data_ptr(), _rows(scales, K // 32), _stream(y))
+    return q, scales
+
+
+# ---- fused pre -------------------------------------------------------------------------------
+def pre_workspace_bytes(M: int, H: int) -> int:
+    return int(_lib.lib().hc_pre_workspace_bytes(M, H))
+
+
+def pre(R: torch.Tensor, fn_packed: torch.Tensor, scale: torch.Tensor, base: torch.Tensor,
+        weight: torch.Tensor, rms_eps: float = RMS_EPS, pre_eps: float = HC_EPS,
+        sinkhorn_eps: float = HC_EPS, iters: int = ITERS, post_mult: float = POST_MULT,
+        norm_eps: float = RMS_EPS, want_pre: bool = False, out=None,
+        workspace: Optional[torch.Tensor] = None):
+    """Fused stages 1-4: (y bf16 [M, H], post [M, 4], comb [M, 4, 4], pre [M, 4] or None)."""
+    M, H, ldR = _residual(R)
+    _contig(scale, "scale", torch.float32, (3,))
+    _contig(base, "base", torch.float32, (MIX,))
+    _contig(weight, "weight", torch.bfloat16, (H,))
+    dev = R.device
+    if out is None:
+        out = (torch.empty(M, H, dtype=torch.bfloat16, device=dev),
+               torch.empty(M, HC, dtype=torch.float32, device=dev),
+               torch.empty(M, HC, HC, dtype=torch.float32, device=dev),
+               torch.empty(M, HC, dtype=torch.float32, device=dev) if want_pre else None)
+    y, post_, comb, pre_ = out
+    _need(y, "y", torch.bfloat16, 2)
+    _contig(post_, "post", torch.float32, (M, HC))
+    _contig(comb, "comb", torch.float32, (M, HC, HC))
+    if pre_ is not None:
+        _contig(pre_, "pre", torch.float32, (M, HC))
+    ws = _workspace(pre_workspace_bytes(M, H), dev, workspace)
+    _lib.call("hc_pre", R.data_ptr(), ldR, fn_packed.data_ptr(), scale.data_ptr(),
+              base.data_ptr(), weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters,
+              post_mult, norm_eps, y.data_ptr(), _rows(y, H), _ptr(pre_), post_.data_ptr(),
+              comb.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(R))
+    return y, post_, comb, pre_

@@ -1,0 +1,174 @@
+/*
+ * hc_mi355x.h - C ABI of the MI355X (gfx950) library for the manifold hyper-connection (mHC)
+ * pre/post path of a DeepSeek-V4-style decoder, on the bf16 [M, 4, H] multi-stream residual.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every data pointer is a DEVICE pointer owned by the caller. The library never allocates
+ *   or frees device memory and never synchronises; each call enqueues its kernels on
+ *   `stream` (a hipStream_t; NULL means the default stream) and returns. Kernel-execution
+ *   errors surface at the caller's next synchronisation.
+ * - bf16 tensors are passed as uint16_t bit patterns; fp32 as float.
+ * - `ld*` arguments are row strides in ELEMENTS of the pointed-to type; inner strides are 1.
+ *   The residual R is [M, 4, H] with the 4 streams of a row contiguous (stream i, column h at
+ *   R[m*ldR + i*H + h]), so ldR >= 4*H.
+ * - Row pointers and row strides of bf16 / u8 tensors must keep 16-byte alignment
+ *   (pointers 16-byte aligned, ld*·sizeof(elem) a multiple of 16).
+ * - Outputs must not overlap inputs.
+ * - M == 0 is a successful no-op. A row slice [a, b) of a call is the same call with every
+ *   row pointer advanced by a rows and M = b - a; the library takes no "logical row count"
+ *   and keys no choice on M, and every row's result is bit-identical whether the row is
+ *   computed in a full call or in any slice.
+ * - Return value: HC_OK (0) or one of the HC_ERR_* codes below; hc_status_string() names it.
+ *   An error return means nothing was enqueued.
+ *
+ * Sources: the three pages the method is taken from, cited by page and section -
+ *   "deepseek_v4.py" (sglang's DeepSeek-V4 model file), "prefill_sp.py" (the prefill
+ *   sequence-parallel adapter) and "test_prefill_sp_gpu.py" (its one-GPU test).
+ */
+#ifndef HC_MI355X_H
+#define HC_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HC_API __attribute__((visibility("default")))
+
+enum {
+  HC_OK = 0,
+  HC_ERR_NULL = 1,       /* a required pointer is NULL while M > 0 */
+  HC_ERR_SHAPE = 2,      /* unsupported H / K / iters, or a row stride shorter than a row */
+  HC_ERR_ALIGN = 3,      /* a pointer or a row stride breaks the 16-byte alignment rule */
+  HC_ERR_ALIAS = 4,      /* an output overlaps an input */
+  HC_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than the matching *_workspace_bytes() */
+  HC_ERR_LAUNCH = 6,     /* HIP reported an error while enqueuing a kernel */
+  HC_ERR_ARG = 7         /* any other bad argument (negative M, M >= 2^31, non-finite eps) */
+};
+
+/* Name of a status code ("HC_OK", "HC_ERR_SHAPE", ...). Never NULL. */
+HC_API const char* hc_status_string(int status);
+
+/* Library ABI version (major*100 + minor). */
+HC_API int hc_abi_version(void);
+
+/* ---------------------------------------------------------------------------------------
+ * Weight preparation: the mix projection fn, split for the matrix cores.
+ *
+ * deepseek_v4.py, make_hc_mixing_params: fn is fp32 [(2+hc)*hc, hc*H] = [24, 4H]. The
+ * DeepGEMM prenorm path of DeepseekV4DecoderLayer.hc_pre contracts it with the bf16
+ * flattened residual. This call rewrites fn once per weight into three bf16 parts
+ * (fn = hi + mid + lo, each part the round-to-nearest-even of what the earlier parts leave),
+ * laid out in the order hc_pre_stats / hc_pre read them. Like the decoder layer's cached
+ * bf16 norm weights (DeepseekV4DecoderLayer.refresh_mhc_norm_weight_cache), it belongs to
+ * weight loading, not to each forward.
+ *
+ * fn:        fp32 [24, 4H] row-major (device).
+ * fn_packed: hc_fn_packed_bytes(H) bytes (device, 16-byte aligned), written.
+ * H:         multiple of 256.
+ * ------------------------------------------------------------------------------------- */
+HC_API size_t hc_fn_packed_bytes(int32_t H);
+HC_API int hc_fn_pack(const float* fn, int32_t H, uint16_t* fn_packed, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Stage 1, mix stats. deepseek_v4.py, DeepseekV4DecoderLayer.hc_pre (hc_pre_torch_impl and
+ * the DeepGEMM prenorm path): with x = R[m] flattened stream-major (4H values),
+ *   sumsq[m] = sum_k x_k^2,  mixes[m, f] = (sum_k fn[f, k] x_k) * rsqrt(sumsq[m] / 4H + rms_eps).
+ *
+ * R:          bf16 [M, 4, H], row stride ldR >= 4H.
+ * fn_packed:  from hc_fn_pack for the same H.
+ * mixes:      fp32 [M, 24], contiguous, written.
+ * sumsq:      fp32 [M] or NULL, written when given.
+ * workspace:  >= hc_pre_stats_workspace_bytes(M, H) bytes of device memory, 256-byte aligned;
+ *             its contents on entry do not matter.
+ * H:          multiple of 256.
+ * ------------------------------------------------------------------------------------- */
+HC_API size_t hc_pre_stats_workspace_bytes(int64_t M, int32_t H);
+HC_API int hc_pre_stats(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, int64_t M,
+                        int32_t H, float rms_eps, float* mixes, float* sumsq,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Stages 2-3, split + Sinkhorn (deepseek_v4.py, DeepseekV4DecoderLayer.hc_pre's
+ * hc_split_sinkhorn call with hc_scale, hc_base, hc_mult = 4, hc_sinkhorn_iters, hc_eps;
+ * the post multiplier is _MHC_POST_MULT_VALUE = 2). Per row, with s = scale, b = base:
+ *   pre[i]   = sigmoid(s[0]*mixes[i]   + b[i])   + pre_eps                     i = 0..3
+ *   post[i]  = post_mult * sigmoid(s[1]*mixes[4+i] + b[4+i])                   i = 0..3
+ *   L[i][j]  = s[2]*mixes[8+4i+j] + b[8+4i+j]    (i = source stream, j = destination)
+ *   P = softmax_j(L) + sinkhorn_eps; P /= (column sums + sinkhorn_eps);
+ *   then iters-1 times: P /= (row sums + eps); P /= (column sums + eps);  comb = P.
+ *
+ * mixes: fp32 [M, 24]; scale fp32 [3]; base fp32 [24]; iters >= 1.
+ * pre, post: fp32 [M, 4]; comb: fp32 [M, 4, 4] (comb[m][i][j]); all contiguous, written.
+ * ------------------------------------------------------------------------------------- */
+HC_API int hc_sinkhorn(const float* mixes, int64_t M, const float* scale, const float* base,
+                       int32_t iters, float pre_eps, float sinkhorn_eps, float post_mult,
+                       float* pre, float* post, float* comb, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Stage 4, combine + RMSNorm (deepseek_v4.py, DeepseekV4DecoderLayer.hc_pre's pre-combine
+ * and the input_layernorm that follows it, fused as the hc_pre docstring describes;
+ * prefill_sp.py, hc_combine_norm_rows passes explicit row strides the same way):
+ *   c[h] = sum_i pre[m, i] * R[m, i, h]   (fp32)
+ *   y[m, h] = bf16_rne( c[h] * rsqrt(mean_h c^2 + eps) * weight[h] )      one rounding.
+ *
+ * R: bf16 [M, 4, H] (ldR); pre: fp32 [M, 4] with row stride ldPre >= 4 (ldPre*4 bytes,
+ * 16-byte aligned); weight: bf16 [H]; y: bf16 [M, H] (ldY >= H), written.
+ * H: 512 * n for n in {1, 2, 4, 8, 10, 14, 16}.
+ * ------------------------------------------------------------------------------------- */
+HC_API int hc_combine_norm(const uint16_t* R, int64_t ldR, const float* pre, int64_t ldPre,
+                           const uint16_t* weight, int64_t M, int32_t H, float eps,
+                           uint16_t* y, int64_t ldY, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Stage 5, hc post (deepseek_v4.py, DeepseekV4DecoderLayer.hc_post, hc_post_torch_impl;
+ * the out-parameter form follows the aiter mhc_post call there):
+ *   Rout[m, j, h] = bf16_rne( post[m, j] * x[m, h] + sum_i comb[m, i, j] * R[m, i, h] ).
+ *
+ * x: bf16 [M, H] (ldX >= H); R: bf16 [M, 4, H] (ldR); post fp32 [M, 4], comb fp32 [M, 4, 4],
+ * contiguous; Rout: bf16 [M, 4, H] (ldOut >= 4H), written. H: multiple of 512.
+ * ------------------------------------------------------------------------------------- */
+HC_API int hc_post(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                   const float* post, const float* comb, int64_t M, int32_t H,
+                   uint16_t* Rout, int64_t ldOut, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Row-local MXFP8 quantizer (prefill_sp.py, module docstring stage 2 and _mxfp8_quantize /
+ * mxfp8_gather: e4m3 values, one ue8m0 scale per row per 32 columns, linear scale layout).
+ * Per 32-column block with maximum magnitude amax: e = the smallest integer with
+ * amax * 2^-e <= 448, clamped to [-127, 127] (all-zero block: -127); scales[m, g] = e + 127;
+ * q[m, k] = e4m3fn round-to-nearest-even of y[m, k] * 2^-e (saturating at +-448, sign of
+ * zero kept). Inputs must be finite.
+ *
+ * y: bf16 [M, K] (ldY >= K); q: u8 [M, K] (ldQ >= K); scales: u8 [M, K/32] (ldS >= K/32,
+ * any alignment). K: multiple of 32.
+ * ------------------------------------------------------------------------------------- */
+HC_API int mxfp8_quant_rows(const uint16_t* y, int64_t ldY, int64_t M, int32_t K,
+                            uint8_t* q, int64_t ldQ, uint8_t* scales, int64_t ldS, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Fused pre: stages 1-4 in two kernels (deepseek_v4.py, DeepseekV4DecoderLayer.hc_pre with a
+ * norm given: mhc_pre(residual, fn, hc_scale, hc_base, rms_eps, hc_pre_eps,
+ * hc_sinkhorn_eps, hc_post_mult_value, sinkhorn_repeat, norm_weight, norm_eps) returns
+ * (post, comb, y) with y already normalised). Same arithmetic, bit for bit, as
+ * hc_pre_stats -> hc_sinkhorn -> hc_combine_norm.
+ *
+ * pre may be NULL (not written); post fp32 [M, 4], comb fp32 [M, 4, 4], y bf16 [M, H] (ldY).
+ * H: as hc_combine_norm and a multiple of 256. workspace: >= hc_pre_workspace_bytes(M, H).
+ * ------------------------------------------------------------------------------------- */
+HC_API size_t hc_pre_workspace_bytes(int64_t M, int32_t H);
+HC_API int hc_pre(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed,
+                  const float* scale, const float* base, const uint16_t* weight,
+                  int64_t M, int32_t H, float rms_eps, float pre_eps, float sinkhorn_eps,
+                  int32_t iters, float post_mult, float norm_eps,
+                  uint16_t* y, int64_t ldY, float* pre, float* post, float* comb,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HC_MI355X_H */

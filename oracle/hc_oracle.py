@@ -152,7 +152,10 @@ def hc_combine(R_bits, pre):
     """c[m, h] = sum_i pre[m, i] * R[m, i, h], float64."""
     R = bf16_to_f64(R_bits)
     pre = np.asarray(pre, dtype=np.float64)
-    return np.einsum("mi,mih->mh", pre, R)
+    c = np.zeros((R.shape[0], R.shape[2]))
+    for i in range(R.shape[1]):
+        c += pre[:, i, None] * R[:, i, :]
+    return c
 
 
 def hc_combine_norm(R_bits, pre, w_bits, eps: float = RMS_EPS):
@@ -174,7 +177,9 @@ def hc_post(x_bits, R_bits, post, comb):
     R = bf16_to_f64(R_bits)
     post = np.asarray(post, dtype=np.float64)
     comb = np.asarray(comb, dtype=np.float64)
-    out = post[:, :, None] * x[:, None, :] + np.einsum("mij,mih->mjh", comb, R)
+    out = post[:, :, None] * x[:, None, :]
+    for i in range(R.shape[1]):  # source stream i feeds every destination j with comb[m, i, j]
+        out += comb[:, i, :, None] * R[:, i, None, :]
     return out, f64_to_bf16(out)
 
 

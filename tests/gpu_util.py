@@ -1,0 +1,76 @@
+"""Helpers shared by the GPU tests: device transfer, oracle-side tolerance checks and the
+workload recipes (shapes, seeds, distributions of the five configurations)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from hyper_connection_residual_hc_amd import inputs
+from oracle import hc_oracle as o
+
+DEV = "cuda"
+H = inputs.H
+
+# tolerances: bf16 outputs |g - o| <= 2e-2 |o| + 1e-3 rms(o_row); fp32 mixes per-row
+# normwise max|g - o| / max|o| <= 1e-5; pre / post / comb max |g - o| <= 1e-5
+BF16_REL = 2e-2
+BF16_ROW_ABS = 1e-3
+STATS_NORMWISE = 1e-5
+COEF_ABS = 1e-5
+
+
+def say(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def dev(t: torch.Tensor) -> torch.Tensor:
+    return t.to(DEV, non_blocking=False).contiguous()
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    """uint16 bit patterns of a (device or host) bf16 tensor."""
+    return inputs.bits(t.detach().cpu())
+
+
+def f32_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def assert_bf16_close(gpu_bits: np.ndarray, oracle: np.ndarray, what: str) -> None:
+    g = o.bf16_to_f64(gpu_bits)
+    rms = np.sqrt(np.mean(oracle * oracle, axis=-1, keepdims=True))
+    bound = BF16_REL * np.abs(oracle) + BF16_ROW_ABS * rms
+    err = np.abs(g - oracle)
+    bad = err > bound
+    assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements out of tolerance; worst "
+                           f"{float((err - bound).max()):.3g} at {np.unravel_index(np.argmax(err - bound), err.shape)}")
+
+
+def assert_mixes_close(gpu: np.ndarray, oracle: np.ndarray, what: str = "mixes") -> None:
+    err = np.max(np.abs(gpu - oracle), axis=-1)
+    scale = np.max(np.abs(oracle), axis=-1)
+    rel = err / np.maximum(scale, 1e-30)
+    assert np.all(rel <= STATS_NORMWISE), f"{what}: worst normwise {rel.max():.3g} (row {rel.argmax()})"
+
+
+def assert_coef_close(gpu: np.ndarray, oracle: np.ndarray, what: str) -> None:
+    err = np.abs(gpu - oracle)
+    assert np.all(err <= COEF_ABS), f"{what}: worst abs {err.max():.3g}"
+
+
+class Site:
+    """One hc site's parameters on host and device (fn, scale, base, norm weight, packed fn)."""
+
+    def __init__(self, param_seed: int, norm_seed: int, H_: int = H):
+        from hyper_connection_residual_hc_amd import ops
+        self.fn, self.scale, self.base = inputs.hc_params(param_seed, H=H_)
+        self.w = inputs.norm_weight(norm_seed, H=H_)
+        self.fn_d, self.scale_d, self.base_d, self.w_d = map(dev, (self.fn, self.scale, self.base, self.w))
+        self.fnp = ops.fn_pack(self.fn_d)
+
+    def oracle_pre(self, R_bits):
+        return o.hc_pre(R_bits, self.fn.numpy(), self.scale.numpy(), self.base.numpy(),
+                        inputs.bits(self.w))

@@ -1,0 +1,80 @@
+"""The C-ABI library loads without a GPU, exports every entry point include/hc_mi355x.h
+declares, and its host-side argument checks return the documented status codes. None of these
+calls reaches a kernel launch (each fails validation or is an M = 0 no-op)."""
+import ctypes
+import os
+
+import pytest
+
+from hyper_connection_residual_hc_amd import _lib
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from hyper_connection_residual_hc_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def test_every_header_symbol_is_exported(L):
+    names = _lib.header_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_no_extra_exports_beyond_the_header(L):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    ours = {n for n in exported if n.startswith(("hc_", "mxfp8_"))}
+    assert ours == set(_lib.header_symbols())
+
+
+def test_status_strings(L):
+    assert L.hc_status_string(0) == b"HC_OK"
+    assert L.hc_status_string(2) == b"HC_ERR_SHAPE"
+    assert L.hc_status_string(99) == b"HC_ERR_UNKNOWN"
+    assert L.hc_abi_version() == 100
+
+
+def test_sizes(L):
+    H = 5120
+    assert L.hc_fn_packed_bytes(H) == 8 * 4 * (H // 256) * 5 * 64 * 8 * 2
+    assert L.hc_fn_packed_bytes(100) == 0
+    assert L.hc_pre_stats_workspace_bytes(4096, H) == 8 * 4096 * 32 * 4
+    assert L.hc_pre_workspace_bytes(0, H) == 0
+    assert L.hc_pre_stats_workspace_bytes(-1, H) == 0
+
+
+def test_validation_codes(L):
+    H = 5120
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+    # M = 0 is a no-op, even with NULL pointers
+    assert L.hc_post(None, 0, None, 0, None, None, 0, H, None, 0, None) == 0
+    assert L.hc_combine_norm(None, 0, None, 0, None, 0, H, 1e-6, None, 0, None) == 0
+    assert L.mxfp8_quant_rows(None, 0, 0, H, None, 0, None, 0, None) == 0
+    # NULL pointers with M > 0
+    assert L.hc_post(None, H, None, 4 * H, None, None, 5, H, None, 4 * H, None) == 1
+    assert L.hc_sinkhorn(None, 3, None, None, 20, 1e-6, 1e-6, 2.0, None, None, None, None) == 1
+    # shapes
+    assert L.hc_post(fake, H, fake, 4 * H, fake, fake, 5, 640, fake, 4 * H, None) == 2
+    assert L.hc_combine_norm(fake, 4 * H, fake, 4, fake, 5, 3 * 512, 1e-6, fake, H, None) == 2
+    assert L.hc_sinkhorn(fake, 3, fake, fake, 0, 1e-6, 1e-6, 2.0, fake, fake, fake, None) == 2
+    assert L.mxfp8_quant_rows(fake, 40, 2, 40, fake, 40, fake, 1, None) == 2
+    assert L.hc_post(fake, H, fake, 4 * H - 8, fake, fake, 5, H, fake, 4 * H, None) == 2
+    # arguments
+    assert L.hc_post(fake, H, fake, 4 * H, fake, fake, -1, H, fake, 4 * H, None) == 7
+    assert L.hc_combine_norm(fake, 4 * H, fake, 4, fake, 5, H, float("nan"), fake, H, None) == 7
+    # alignment: a 2-byte offset pointer
+    mis = ctypes.c_void_p(0x10002)
+    assert L.hc_post(mis, H, fake, 4 * H, fake, fake, 5, H, fake, 4 * H, None) == 3
+    # aliasing: output over the input residual
+    assert L.hc_post(ctypes.c_void_p(0x900000), H, fake, 4 * H, ctypes.c_void_p(0xA00000),
+                     ctypes.c_void_p(0xB00000), 5, H, fake, 4 * H, None) == 4
+    # workspace too small
+    assert L.hc_pre_stats(fake, 4 * H, fake, 5, H, 1e-6, ctypes.c_void_p(0x800000), None,
+                          ctypes.c_void_p(0x700000), 16, None) == 5

@@ -1,0 +1,223 @@
+"""GPU parity of every C-ABI entry point against the CPU oracle, element by element, on seeded
+inputs with the workload's distributions (several tiles plus a ragged tail), and the edge
+cases: empty calls, single rows, zero rows, poisoned outputs, untouched inputs."""
+import numpy as np
+import pytest
+import torch
+
+from hyper_connection_residual_hc_amd import inputs, ops
+from oracle import hc_oracle as o
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def attn():
+    return gu.Site(inputs.SEED_ATTN, inputs.SEED_NORM_ATTN)
+
+
+def _poison_f32(*shape):
+    return torch.full(shape, float("nan"), dtype=torch.float32, device=gu.DEV)
+
+
+def _poison_bf16(*shape):
+    return torch.full(shape, -1, dtype=torch.int16, device=gu.DEV).view(torch.bfloat16)
+
+
+# ------------------------------------------------------------------------------------------
+def test_fn_pack_reconstructs_fn(attn):
+    """The packed hi/mid/lo parts sum back to fn within 2^-24 relative (three bf16 parts)."""
+    gu.say("fn_pack H=5120 seed=11")
+    p = o.bf16_to_f64(attn.fnp.cpu().numpy().view(np.uint16))
+    NC = gu.H // 256
+    p = p.reshape(8, 4, NC, 5, 4, 16, 8)  # s, w, c, t, g, n, e
+    fn = attn.fn.numpy().astype(np.float64)
+    rebuilt = np.zeros_like(fn)
+    for t in range(5):
+        for n in range(16):
+            col = 16 * t + n
+            if col >= 72:
+                assert np.all(p[:, :, :, t, :, n, :] == 0)
+                continue
+            f = col % 24
+            blk = p[:, :, :, t, :, n, :]  # s, w, c, g, e -> k = w*H + s*H/8 + 32c + 8g + e
+            k_idx = (np.arange(4)[None, :, None, None, None] * gu.H
+                     + np.arange(8)[:, None, None, None, None] * (gu.H // 8)
+                     + 32 * np.arange(NC)[None, None, :, None, None]
+                     + 8 * np.arange(4)[None, None, None, :, None]
+                     + np.arange(8)[None, None, None, None, :])
+            rebuilt[f, k_idx.reshape(-1)] += blk.reshape(-1)
+    np.testing.assert_allclose(rebuilt, fn, rtol=2.0**-22, atol=0)
+
+
+@pytest.mark.parametrize("M", [128, 300, 1500])
+def test_pre_stats_matches_oracle(attn, M):
+    gu.say(f"hc_pre_stats M={M} seed={M}")
+    R = inputs.residual(M, M)
+    mixes, sumsq = ops.pre_stats(gu.dev(R), attn.fnp, mixes=_poison_f32(M, 24),
+                                 sumsq=_poison_f32(M))
+    om, osq = o.hc_mix_stats(inputs.bits(R), attn.fn.numpy())
+    gu.assert_mixes_close(gu.f32_np(mixes), om)
+    np.testing.assert_allclose(gu.f32_np(sumsq), osq, rtol=2e-6)
+
+
+@pytest.mark.parametrize("M", [1, 77, 1024])
+def test_sinkhorn_matches_oracle(attn, M):
+    gu.say(f"hc_sinkhorn M={M}")
+    R = inputs.residual(M, M + 7)
+    om, _ = o.hc_mix_stats(inputs.bits(R), attn.fn.numpy())
+    mixes32 = torch.from_numpy(om.astype(np.float32))
+    pre, post, comb = ops.sinkhorn(gu.dev(mixes32), attn.scale_d, attn.base_d,
+                                   out=(_poison_f32(M, 4), _poison_f32(M, 4), _poison_f32(M, 4, 4)))
+    opre, opost, ocomb = o.hc_split_sinkhorn(mixes32.numpy(), attn.scale.numpy(), attn.base.numpy())
+    gu.assert_coef_close(gu.f32_np(pre), opre, "pre")
+    gu.assert_coef_close(gu.f32_np(post), opost, "post")
+    gu.assert_coef_close(gu.f32_np(comb), ocomb, "comb")
+
+
+@pytest.mark.parametrize("M", [1, 130, 1500])
+def test_combine_norm_matches_oracle(attn, M):
+    gu.say(f"hc_combine_norm M={M}")
+    R = inputs.residual(M, M + 11)
+    pre = torch.rand(M, 4, generator=torch.Generator().manual_seed(M)) + 1e-6
+    y = ops.combine_norm(gu.dev(R), gu.dev(pre), attn.w_d, out=_poison_bf16(M, gu.H))
+    oy, _ = o.hc_combine_norm(inputs.bits(R), pre.numpy(), inputs.bits(attn.w))
+    gu.assert_bf16_close(gu.bits_of(y), oy, "y")
+
+
+def test_combine_norm_strided_pre(attn):
+    M = 64
+    R = inputs.residual(M, 5)
+    pre_wide = torch.rand(M, 8, generator=torch.Generator().manual_seed(3))
+    y = ops.combine_norm(gu.dev(R), gu.dev(pre_wide)[:, 2:6], attn.w_d)
+    oy, _ = o.hc_combine_norm(inputs.bits(R), pre_wide[:, 2:6].numpy(), inputs.bits(attn.w))
+    gu.assert_bf16_close(gu.bits_of(y), oy, "y (strided pre)")
+
+
+@pytest.mark.parametrize("M", [1, 333, 4096])
+def test_post_matches_oracle(attn, M):
+    """Config 2 at M=4096: post and comb from the config-0-style parameters on R."""
+    gu.say(f"hc_post M={M} seed={M}")
+    R = inputs.residual(M, M)
+    x = inputs.sublayer_out(M, M + 1)
+    ref = attn.oracle_pre(inputs.bits(R))
+    post32 = torch.from_numpy(ref["post"].astype(np.float32))
+    comb32 = torch.from_numpy(ref["comb"].astype(np.float32))
+    out = ops.post(gu.dev(x), gu.dev(R), gu.dev(post32), gu.dev(comb32),
+                   out=_poison_bf16(M, 4, gu.H))
+    oR, _ = o.hc_post(inputs.bits(x), inputs.bits(R), post32.numpy(), comb32.numpy())
+    gu.assert_bf16_close(gu.bits_of(out), oR, "R'")
+
+
+@pytest.mark.parametrize("M", [128, 2048])
+def test_fused_pre_matches_oracle_and_unfused(attn, M):
+    """Config 0 (M=128) and config 1 (M=2048): the fused pre against the oracle, and bit for
+    bit against the chain of the separate entry points."""
+    gu.say(f"hc_pre fused M={M} seed={M}")
+    R = inputs.residual(M, M)
+    Rd = gu.dev(R)
+    y, post, comb, pre = ops.pre(Rd, attn.fnp, attn.scale_d, attn.base_d, attn.w_d, want_pre=True,
+                                 out=(_poison_bf16(M, gu.H), _poison_f32(M, 4),
+                                      _poison_f32(M, 4, 4), _poison_f32(M, 4)))
+    ref = attn.oracle_pre(inputs.bits(R))
+    gu.assert_coef_close(gu.f32_np(pre), ref["pre"], "pre")
+    gu.assert_coef_close(gu.f32_np(post), ref["post"], "post")
+    gu.assert_coef_close(gu.f32_np(comb), ref["comb"], "comb")
+    gu.assert_bf16_close(gu.bits_of(y), ref["y"], "y")
+    # separate entry points give the same bits
+    mixes, _ = ops.pre_stats(Rd, attn.fnp)
+    pre2, post2, comb2 = ops.sinkhorn(mixes, attn.scale_d, attn.base_d)
+    y2 = ops.combine_norm(Rd, pre2, attn.w_d)
+    assert torch.equal(pre, pre2) and torch.equal(post, post2) and torch.equal(comb, comb2)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+def test_sinkhorn_outputs_are_column_stochastic(attn):
+    M = 512
+    R = inputs.residual(M, 99)
+    _, _, comb, _ = ops.pre(gu.dev(R), attn.fnp, attn.scale_d, attn.base_d, attn.w_d)
+    col = comb.double().sum(dim=1)
+    assert torch.all((col - 1).abs() < 1e-5)
+    assert torch.all(comb > 0)
+
+
+# ------------------------------------------------------------------------------------------
+# edge cases
+# ------------------------------------------------------------------------------------------
+def test_empty_calls_are_noops(attn):
+    R = torch.empty(0, 4, gu.H, dtype=torch.bfloat16, device=gu.DEV)
+    y, post, comb, _ = ops.pre(R, attn.fnp, attn.scale_d, attn.base_d, attn.w_d)
+    assert y.shape == (0, gu.H) and post.shape == (0, 4) and comb.shape == (0, 4, 4)
+    out = ops.post(torch.empty(0, gu.H, dtype=torch.bfloat16, device=gu.DEV), R,
+                   torch.empty(0, 4, device=gu.DEV), torch.empty(0, 4, 4, device=gu.DEV))
+    assert out.shape == (0, 4, gu.H)
+    q, s = ops.mxfp8_quant_rows(torch.empty(0, gu.H, dtype=torch.bfloat16, device=gu.DEV))
+    assert q.shape == (0, gu.H) and s.shape == (0, gu.H // 32)
+    torch.cuda.synchronize()
+
+
+def test_zero_rows(attn):
+    """An all-zero residual row: mixes 0, so pre/post/comb come from base alone and y = 0."""
+    M = 20
+    R = inputs.residual(M, 31)
+    R[3] = 0
+    R[17] = 0
+    y, post, comb, pre = ops.pre(gu.dev(R), attn.fnp, attn.scale_d, attn.base_d, attn.w_d,
+                                 want_pre=True)
+    ref = attn.oracle_pre(inputs.bits(R))
+    assert np.all(ref["mixes"][[3, 17]] == 0)
+    gu.assert_coef_close(gu.f32_np(pre), ref["pre"], "pre")
+    gu.assert_coef_close(gu.f32_np(comb), ref["comb"], "comb")
+    yb = gu.bits_of(y)
+    assert np.all((yb[[3, 17]] & 0x7FFF) == 0)
+    gu.assert_bf16_close(yb, ref["y"], "y")
+
+
+def test_inputs_are_not_modified(attn):
+    M = 257
+    R = gu.dev(inputs.residual(M, 41))
+    x = gu.dev(inputs.sublayer_out(M, 42))
+    R0, x0 = R.clone(), x.clone()
+    fnp0 = attn.fnp.clone()
+    y, post, comb, _ = ops.pre(R, attn.fnp, attn.scale_d, attn.base_d, attn.w_d)
+    ops.post(x, R, post, comb)
+    ops.mxfp8_quant_rows(y)
+    torch.cuda.synchronize()
+    assert torch.equal(R.view(torch.int16), R0.view(torch.int16))
+    assert torch.equal(x.view(torch.int16), x0.view(torch.int16))
+    assert torch.equal(attn.fnp, fnp0)
+
+
+def test_error_codes_reach_python(attn):
+    from hyper_connection_residual_hc_amd._lib import HCError
+    R = gu.dev(inputs.residual(8, 1))
+    with pytest.raises(HCError, match="HC_ERR_ALIAS"):
+        ops.combine_norm(R, gu.dev(torch.rand(8, 4)), attn.w_d,
+                         out=R.view(8, -1)[:, : gu.H])
+    raw = torch.empty(8 * 4 * gu.H + 8, dtype=torch.bfloat16, device=gu.DEV)
+    Rmis = raw[1:1 + 8 * 4 * gu.H].view(8, 4, gu.H)  # 2-byte offset: not 16-byte aligned
+    with pytest.raises(HCError, match="HC_ERR_ALIGN"):
+        ops.combine_norm(Rmis, gu.dev(torch.rand(8, 4)), attn.w_d)
+    with pytest.raises(HCError, match="HC_ERR_SHAPE"):
+        ops.post(gu.dev(inputs.sublayer_out(2, 1, H=640)), gu.dev(inputs.residual(2, 1, H=640)),
+                 gu.dev(torch.rand(2, 4)), gu.dev(torch.rand(2, 4, 4)))
+
+
+def test_small_hidden_size():
+    """H = 512: one column block per lane group, one 64-column slice per stream and XCD."""
+    Hs = 512
+    site = gu.Site(5, 6, H_=Hs)
+    M = 70
+    R = inputs.residual(M, 8, H=Hs)
+    y, post, comb, pre = ops.pre(gu.dev(R), site.fnp, site.scale_d, site.base_d, site.w_d,
+                                 want_pre=True)
+    ref = site.oracle_pre(inputs.bits(R))
+    gu.assert_coef_close(gu.f32_np(comb), ref["comb"], "comb")
+    gu.assert_bf16_close(gu.bits_of(y), ref["y"], "y")
+    x = inputs.sublayer_out(M, 9, H=Hs)
+    post32 = torch.from_numpy(ref["post"].astype(np.float32))
+    comb32 = torch.from_numpy(ref["comb"].astype(np.float32))
+    out = ops.post(gu.dev(x), gu.dev(R), gu.dev(post32), gu.dev(comb32))
+    oR, _ = o.hc_post(inputs.bits(x), inputs.bits(R), post32.numpy(), comb32.numpy())
+    gu.assert_bf16_close(gu.bits_of(out), oR, "R'")
