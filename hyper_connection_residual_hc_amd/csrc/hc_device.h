@@ -129,15 +129,16 @@ __device__ __forceinline__ float split_sinkhorn_lane(int e, float mix_a, float m
     *prepost = sp.post_mult * sigmoidf_(__fmaf_rn(sp.s1, mix_a, base_a));
   }
   float L = __fmaf_rn(sp.s2, mix_c, base_c);
-  // softmax over j (the quad), then + eps on every entry
+  // softmax over j (the quad), then + eps on every entry. Each normalisation multiplies by
+  // v_rcp_f32 of (sum + eps) (reciprocal within 1 ulp).
   float mx = quad_max(L);
   float ex = expf(L - mx);
-  float p = ex / quad_sum(ex) + sp.sk_eps;
+  float p = ex * __builtin_amdgcn_rcpf(quad_sum(ex)) + sp.sk_eps;
   // first column step
-  p = p / (stride4_sum(p) + sp.sk_eps);
+  p = p * __builtin_amdgcn_rcpf(stride4_sum(p) + sp.sk_eps);
   for (int it = 1; it < sp.iters; ++it) {
-    p = p / (quad_sum(p) + sp.sk_eps);     // rows: sum over j
-    p = p / (stride4_sum(p) + sp.sk_eps);  // columns: sum over i
+    p = p * __builtin_amdgcn_rcpf(quad_sum(p) + sp.sk_eps);     // rows: sum over j
+    p = p * __builtin_amdgcn_rcpf(stride4_sum(p) + sp.sk_eps);  // columns: sum over i
   }
   return p;
 }

@@ -9,14 +9,14 @@
 
 namespace hc {
 
-// Stats split-K geometry: 8 column slices (one per XCD when the grid's block index is taken
-// modulo 8), each slice = H/8 columns of every stream; 32-column chunks inside a slice;
-// 5 B-operand tiles of 16 packed columns (hi | mid | lo parts of the 24 fn rows, padded to 80).
+// Stats split-K geometry: 8 contiguous slices of the 4H flattened columns (one per XCD when
+// the grid's block index is taken modulo 8); 32-column chunks inside a slice; 5 B-operand
+// tiles of 16 packed columns (hi | mid | lo parts of the 24 fn rows, padded to 80).
 constexpr int kSlices = 8;
 constexpr int kPackTiles = 5;
 constexpr int kStatsRows = 64;        // rows per stats workgroup
 constexpr int kPartStride = 32;       // floats per (slice, row) partial record: 24 dots + sumsq
-inline int64_t packed_fn_elems(int H) { return (int64_t)kSlices * kHC * (H / 256) * kPackTiles * 64 * 8; }
+inline int64_t packed_fn_elems(int H) { return (int64_t)kSlices * (H / 64) * kPackTiles * 64 * 8; }
 inline size_t stats_workspace_bytes(int64_t M) { return (size_t)kSlices * (size_t)M * kPartStride * 4; }
 
 // Sum of one field of a row's 8 slice partials, in slice order 0..7. Used by every consumer

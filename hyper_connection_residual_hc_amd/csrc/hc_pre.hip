@@ -54,24 +54,31 @@ hipError_t launch_sinkhorn(const float* mixes, int M, const float* scale, const 
 // ---- combine + RMSNorm of one row by one wavefront ------------------------------------------
 // NG = H / 512 column blocks; lane covers columns [512 g + 8 lane, +8) of each block g.
 template <int NG>
-__device__ __forceinline__ void combine_norm_row(const uint16_t* __restrict__ Rr,
-                                                 const float (&p)[kHC],
-                                                 const uint16_t* __restrict__ w, float eps,
-                                                 uint16_t* __restrict__ yr, int lane) {
+struct RowTile {
+  u32x4 r[NG][kHC];
+};
+
+template <int NG>
+__device__ __forceinline__ void load_row(const uint16_t* __restrict__ Rr, int lane, RowTile<NG>& t) {
   constexpr int H = NG * 512;
-  u32x4 rv[NG][kHC];
 #pragma unroll
   for (int g = 0; g < NG; ++g)
 #pragma unroll
-    for (int i = 0; i < kHC; ++i) rv[g][i] = ld16_stream(Rr + i * H + g * 512 + lane * 8);
+    for (int i = 0; i < kHC; ++i) t.r[g][i] = ld16_stream(Rr + i * H + g * 512 + lane * 8);
+}
 
+template <int NG>
+__device__ __forceinline__ void combine_norm_row(const RowTile<NG>& t, const float (&p)[kHC],
+                                                 const uint16_t* __restrict__ w, float eps,
+                                                 uint16_t* __restrict__ yr, int lane) {
+  constexpr int H = NG * 512;
   float c[NG][8];
   float ss = 0.0f;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     float r[kHC][8];
 #pragma unroll
-    for (int i = 0; i < kHC; ++i) unpack8(rv[g][i], r[i]);
+    for (int i = 0; i < kHC; ++i) unpack8(t.r[g][i], r[i]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float a = p[0] * r[0][e];
@@ -104,10 +111,12 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const uint16_t* __res
   const int lane = threadIdx.x & 63;
   const int m = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
   if (m >= M) return;
+  RowTile<NG> t;
+  load_row<NG>(R + (int64_t)m * ldR, lane, t);
   float p[kHC];
 #pragma unroll
   for (int i = 0; i < kHC; ++i) p[i] = pre[(int64_t)m * ldPre + i];
-  combine_norm_row<NG>(R + (int64_t)m * ldR, p, w, eps, y + (int64_t)m * ldY, lane);
+  combine_norm_row<NG>(t, p, w, eps, y + (int64_t)m * ldY, lane);
 }
 
 // ---- fused: slice reduce + split + Sinkhorn + combine + RMSNorm ----------------------------
@@ -122,6 +131,9 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(
   const int m = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
   if (m >= M) return;  // wave-uniform: the whole wave leaves together
   const int e = lane & 15;
+  // the row's residual loads go out first; the split + Sinkhorn below hides their latency
+  RowTile<NG> t;
+  load_row<NG>(R + (int64_t)m * ldR, lane, t);
 
   // mixes for this lane's entries, reduced over the slices exactly as stats_reduce does
   const float ss = slice_sum(part, M, m, kMix);
@@ -143,7 +155,7 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(
   float p[kHC];
 #pragma unroll
   for (int i = 0; i < kHC; ++i) p[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), i));
-  combine_norm_row<NG>(R + (int64_t)m * ldR, p, w, norm_eps, y + (int64_t)m * ldY, lane);
+  combine_norm_row<NG>(t, p, w, norm_eps, y + (int64_t)m * ldY, lane);
 }
 
 // ---- dispatch over the compiled H values ----------------------------------------------------
