@@ -37,7 +37,7 @@ int launched(hipError_t err) { return err == hipSuccess ? HC_OK : HC_ERR_LAUNCH;
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-bool stats_h_ok(int32_t H) { return H > 0 && H % 1024 == 0 && H <= (1 << 20); }
+bool stats_h_ok(int32_t H) { return H > 0 && H % 512 == 0 && H <= (1 << 20); }
 bool post_h_ok(int32_t H) { return H > 0 && H % 512 == 0 && H <= (1 << 20); }
 
 // R [M, 4, H] bf16 with row stride ldR

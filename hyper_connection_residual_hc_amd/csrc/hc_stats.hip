@@ -14,14 +14,14 @@
 // Gram tile).
 //
 // Memory: the MFMA operand layout wants 16 rows x 64 bytes per wave instruction, which streams
-// HBM poorly; so each block stages 64 rows x 1 KB of its column slice through LDS. A wave loads
-// 16 of the rows with 1 KB wave-wide loads, writes them to a padded LDS tile (row stride
-// 1040 B: conflict-free 16-byte reads), and after a barrier reads 16 x 64-byte operand tiles
-// back. The next stage's loads are in flight while the current stage is multiplied.
+// HBM poorly; so each block stages 64 rows x 512 B of its column slice through LDS. A wave
+// loads 16 of the rows with wave-wide loads of 2 rows x 512 B, writes them to a padded LDS tile
+// (row stride 528 B: conflict-free 16-byte reads), and after a barrier reads 64-byte operand
+// tiles back. The next stage's loads are in flight while the current stage is multiplied.
 //
 // Split-K: 8 contiguous column slices of 4H/8 flattened columns; block b takes slice b % 8, so
 // with round-robin dispatch each XCD keeps one slice of packed fn (1/8 of 3.3 MB) in its L2.
-// A block owns 64 rows; wave q multiplies chunks 4q..4q+3 of every 16-chunk stage for all 64
+// A block owns 64 rows; wave q multiplies chunks 2q, 2q+1 of every 8-chunk stage for all 64
 // rows (the fn operand of a chunk serves 64 rows). Partials go to a workspace [8][M][32] and
 // are summed in slice order 0..7 by the consumer. Nothing depends on M or on a row's position
 // in its tile, so any row slice of a call gives identical bits.
@@ -96,9 +96,10 @@ hipError_t launch_fn_pack(const float* fn, int H, uint16_t* fn_packed, hipStream
 
 // ---- split-K stats -------------------------------------------------------------------------
 constexpr int kSub = kStatsRows / 16;       // 16-row MFMA subtiles per block
-constexpr int kStageElems = 512;            // columns of a row per stage (1 KB)
+constexpr int kStageElems = 256;            // columns of a row per stage (512 B)
 constexpr int kStageChunks = kStageElems / 32;
-constexpr int kLdsRow = kStageElems + 8;    // padded LDS row stride in elements (1040 B)
+constexpr int kWaveChunks = kStageChunks / 4;  // chunks each wave multiplies per stage
+constexpr int kLdsRow = kStageElems + 8;    // padded LDS row stride in elements (528 B)
 constexpr int kLdsCols = 33;                // epilogue: 32 accumulator columns + sumsq
 
 struct StatsAcc {
@@ -132,16 +133,19 @@ __global__ __launch_bounds__(256) void stats_kernel(const uint16_t* __restrict__
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const int NCS = H >> 6;            // chunks per slice
-  const int nstage = H >> 10;        // 1 KB stages per slice row
-  const uint16_t* rbase = R + (int64_t)s * (H / 2) + lane * 8;
+  const int nstage = H >> 9;         // 512-byte stages per slice row
+  // a wave instruction loads 512 B of two rows: lanes 0..31 the first, 32..63 the second
+  const int half = lane >> 5;
+  const int col = (lane & 31) * 8;
+  const uint16_t* rbase = R + (int64_t)s * (H / 2) + col;
   const u32x4* bbase = reinterpret_cast<const u32x4*>(fnp) + (int64_t)s * NCS * kPackTiles * 64 + lane;
 
   // stage loads: wave q brings rows 16q .. 16q+15 (rows past the end re-read row M-1)
-  u32x4 L[16];
+  u32x4 L[8];
   auto issue = [&](int p) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = min(row0 + 16 * q + i, M - 1);
+    for (int i = 0; i < 8; ++i) {
+      const int row = min(row0 + 16 * q + 2 * i + half, M - 1);
       L[i] = ld16_stream(rbase + (int64_t)row * ldR + p * kStageElems);
     }
   };
@@ -158,23 +162,23 @@ __global__ __launch_bounds__(256) void stats_kernel(const uint16_t* __restrict__
   // (when `next`) the following stage's loads are in flight
   auto stage = [&](int p, bool next) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      *reinterpret_cast<u32x4*>(&lds[(16 * q + i) * kLdsRow + lane * 8]) = L[i];
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(&lds[(16 * q + 2 * i + half) * kLdsRow + col]) = L[i];
     __syncthreads();
     // the fn operands of this stage go out before the next stage's residual loads: loads
     // return in order, so waiting for them does not wait for HBM
-    u32x4 b[4][kPackTiles];
+    u32x4 b[kWaveChunks][kPackTiles];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+    for (int jj = 0; jj < kWaveChunks; ++jj)
 #pragma unroll
       for (int t = 0; t < kPackTiles; ++t)
-        b[jj][t] = bbase[((int64_t)(p * kStageChunks + 4 * q + jj) * kPackTiles + t) * 64];
+        b[jj][t] = bbase[((int64_t)(p * kStageChunks + kWaveChunks * q + jj) * kPackTiles + t) * 64];
     __builtin_amdgcn_sched_barrier(0);
     if (next) issue(p + 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = 4 * q + jj;
+    for (int jj = 0; jj < kWaveChunks; ++jj) {
+      const int j = kWaveChunks * q + jj;
       u32x4 a[kSub];
 #pragma unroll
       for (int sub = 0; sub < kSub; ++sub)
