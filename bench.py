@@ -76,6 +76,9 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
+                    help="fused: hc_post_pre (post with the next pre's mix stats in one pass, "
+                         "then the pre finish); unfused: hc_post then hc_pre")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the mHC path is row-local and this build has no "
@@ -115,11 +118,17 @@ def main() -> int:
         R, x, post, comb, o = sets[k % len(sets)]
         if ev is not None:
             ev[0].record()
-        ops.post(x, R, post, comb, out=o["R1"])
-        if ev is not None:
-            ev[1].record()
-        ops.pre(o["R1"], fnp_f, sc_f, ba_f, w_f, out=(o["y"], o["post"], o["comb"], None),
-                workspace=o["ws"])
+        if args.path == "fused":
+            ops.post_pre(x, R, post, comb, fnp_f, sc_f, ba_f, w_f,
+                         out=(o["R1"], o["y"], o["post"], o["comb"], None), workspace=o["ws"])
+            if ev is not None:
+                ev[1].record()
+        else:
+            ops.post(x, R, post, comb, out=o["R1"])
+            if ev is not None:
+                ev[1].record()
+            ops.pre(o["R1"], fnp_f, sc_f, ba_f, w_f, out=(o["y"], o["post"], o["comb"], None),
+                    workspace=o["ws"])
         if ev is not None:
             ev[2].record()
 

@@ -36,6 +36,10 @@ SIGNATURES = {
     "hc_pre_workspace_bytes": (_sz, [_i64, _i32]),
     "hc_pre": (_int, [_p, _i64, _p, _p, _p, _p, _i64, _i32, _f32, _f32, _f32, _i32, _f32, _f32,
                       _p, _i64, _p, _p, _p, _p, _sz, _p]),
+    "hc_post_pre_workspace_bytes": (_sz, [_i64, _i32]),
+    "hc_post_pre": (_int, [_p, _i64, _p, _i64, _p, _p, _p, _p, _p, _p, _i64, _i32, _f32, _f32,
+                           _f32, _i32, _f32, _f32, _p, _i64, _p, _i64, _p, _p, _p, _p, _sz,
+                           _p]),
 }
 
 _LIB = None

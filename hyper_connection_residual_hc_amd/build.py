@@ -17,7 +17,7 @@ LIB_NAME = "libhc_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["hc_api.hip", "hc_post.hip", "hc_stats.hip", "hc_pre.hip", "mxfp8.hip"]
+SOURCES = ["hc_api.hip", "hc_post.hip", "hc_stats.hip", "hc_pipe.hip", "hc_pre.hip", "mxfp8.hip"]
 
 CXXFLAGS = [
     f"--offload-arch={ARCH}",

@@ -37,7 +37,7 @@ int launched(hipError_t err) { return err == hipSuccess ? HC_OK : HC_ERR_LAUNCH;
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-bool stats_h_ok(int32_t H) { return H > 0 && H % 512 == 0 && H <= (1 << 20); }
+bool stats_h_ok(int32_t H) { return H > 0 && H % 1024 == 0 && H <= (1 << 20); }
 bool post_h_ok(int32_t H) { return H > 0 && H % 512 == 0 && H <= (1 << 20); }
 
 // R [M, 4, H] bf16 with row stride ldR
@@ -255,6 +255,67 @@ HC_API int hc_pre(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, con
   return launched(hc::launch_pre_finish(part, R, ldR, scale, base, weight, (int)M, H, rms_eps,
                                         pre_eps, sinkhorn_eps, iters, post_mult, norm_eps, y, ldY,
                                         pre, post, comb, s));
+}
+
+// ---- fused post -> pre -----------------------------------------------------------------------
+HC_API size_t hc_post_pre_workspace_bytes(int64_t M, int32_t H) {
+  return hc_pre_stats_workspace_bytes(M, H);
+}
+
+HC_API int hc_post_pre(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                       const float* post, const float* comb, const uint16_t* fn_packed,
+                       const float* scale, const float* base, const uint16_t* weight,
+                       int64_t M, int32_t H, float rms_eps, float pre_eps, float sinkhorn_eps,
+                       int32_t iters, float post_mult, float norm_eps, uint16_t* Rout,
+                       int64_t ldOut, uint16_t* y, int64_t ldY, float* pre_out,
+                       float* post_out, float* comb_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if (!stats_h_ok(H) || !hc::combine_h_supported(H) || !post_h_ok(H)) return HC_ERR_SHAPE;
+  if (iters < 1 || iters > 100000) return HC_ERR_SHAPE;
+  if (!finite_nonneg(rms_eps) || !finite_nonneg(pre_eps) || !finite_nonneg(sinkhorn_eps) ||
+      !finite_nonneg(norm_eps) || !isfinite(post_mult))
+    return HC_ERR_ARG;
+  if (M == 0) return HC_OK;
+  if (!x || !R || !post || !comb || !fn_packed || !scale || !base || !weight || !Rout || !y ||
+      !post_out || !comb_out)
+    return HC_ERR_NULL;
+  if ((st = check_residual(R, ldR, H))) return st;
+  if (ldX < H || ldOut < (int64_t)kHC * H || ldY < H) return HC_ERR_SHAPE;
+  if (!al16(x) || !al16(Rout) || !al16(y) || !al16(post) || !al16(comb) || !al16(fn_packed) ||
+      !al16(weight) || (ldX * 2) % 16 || (ldOut * 2) % 16 || (ldY * 2) % 16)
+    return HC_ERR_ALIGN;
+  if (!workspace || workspace_bytes < hc::stats_workspace_bytes(M)) return HC_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return HC_ERR_ALIGN;
+  const Span ins[8] = {rows_span(x, M, ldX, H, 2),
+                       rows_span(R, M, ldR, (int64_t)kHC * H, 2),
+                       rows_span(post, M, kHC, kHC, 4),
+                       rows_span(comb, M, kHC * kHC, kHC * kHC, 4),
+                       Span{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)},
+                       Span{(uintptr_t)scale, (uintptr_t)scale + 12},
+                       Span{(uintptr_t)base, (uintptr_t)base + kMix * 4},
+                       Span{(uintptr_t)weight, (uintptr_t)weight + (uintptr_t)H * 2}};
+  const Span outs[6] = {rows_span(Rout, M, ldOut, (int64_t)kHC * H, 2), rows_span(y, M, ldY, H, 2),
+                        rows_span(post_out, M, kHC, kHC, 4),
+                        rows_span(comb_out, M, kHC * kHC, kHC * kHC, 4),
+                        Span{(uintptr_t)workspace, (uintptr_t)workspace + hc::stats_workspace_bytes(M)},
+                        pre_out ? rows_span(pre_out, M, kHC, kHC, 4) : Span{0, 0}};
+  for (int i = 0; i < 6; ++i) {
+    if (outs[i].b == outs[i].e) continue;
+    for (int j = 0; j < 8; ++j)
+      if (overlaps(outs[i], ins[j])) return HC_ERR_ALIAS;
+    for (int j = i + 1; j < 6; ++j)
+      if (outs[j].b != outs[j].e && overlaps(outs[i], outs[j])) return HC_ERR_ALIAS;
+  }
+  float* part = static_cast<float*>(workspace);
+  hipStream_t s = as_stream(stream);
+  if ((st = launched(hc::launch_post_stats(x, ldX, R, ldR, post, comb, fn_packed, (int)M, H, Rout,
+                                           ldOut, part, s))))
+    return st;
+  return launched(hc::launch_pre_finish(part, Rout, ldOut, scale, base, weight, (int)M, H, rms_eps,
+                                        pre_eps, sinkhorn_eps, iters, post_mult, norm_eps, y, ldY,
+                                        pre_out, post_out, comb_out, s));
 }
 
 }  // extern "C"

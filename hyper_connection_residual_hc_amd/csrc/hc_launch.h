@@ -9,17 +9,19 @@
 
 namespace hc {
 
-// Stats split-K geometry: 8 contiguous slices of the 4H flattened columns (one per XCD when
-// the grid's block index is taken modulo 8); 32-column chunks inside a slice; 5 B-operand
-// tiles of 16 packed columns (hi | mid | lo parts of the 24 fn rows, padded to 80).
+// Stats split-K geometry: 8 column slices (slice s = columns [s*H/8, (s+1)*H/8) of every
+// stream; block b takes slice b % 8, so each XCD keeps one slice's fn in its L2);
+// 32-column chunks inside a slice; 5 B-operand tiles of 16 packed columns (hi | mid | lo
+// parts of the 24 fn rows, padded to 80).
 constexpr int kSlices = 8;
 constexpr int kPackTiles = 5;
-constexpr int kStatsRows = 64;        // rows per stats workgroup
+constexpr int kStatsRows = 64;        // rows per stats tile
 constexpr int kPartStride = 32;       // floats per (slice, row) partial record: 24 dots + sumsq
-inline int64_t packed_fn_elems(int H) { return (int64_t)kSlices * (H / 64) * kPackTiles * 64 * 8; }
+__host__ __device__ inline int64_t chunks_per_slice(int H) { return (int64_t)4 * (H / kSlices) / 32; }
+inline int64_t packed_fn_elems(int H) { return (int64_t)kSlices * chunks_per_slice(H) * kPackTiles * 64 * 8; }
 inline size_t stats_workspace_bytes(int64_t M) { return (size_t)kSlices * (size_t)M * kPartStride * 4; }
 
-// Sum of one field of a row's 8 slice partials, in slice order 0..7. Used by every consumer
+// Sum of one field of a row's slice partials, in slice order. Used by every consumer
 // of the partials, so the standalone and the fused pre give identical bits.
 __device__ __forceinline__ float slice_sum(const float* __restrict__ part, int M, int m, int f) {
   float v = 0.0f;
@@ -33,6 +35,11 @@ hipError_t launch_stats(const uint16_t* R, int64_t ldR, const uint16_t* fn_packe
                         float* part, hipStream_t s);
 hipError_t launch_stats_reduce(const float* part, int M, int H, float rms_eps, float* mixes,
                                float* sumsq, hipStream_t s);
+// hc post fused with the mix stats of its output R' (partials as launch_stats writes them)
+hipError_t launch_post_stats(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                             const float* post, const float* comb, const uint16_t* fn_packed,
+                             int M, int H, uint16_t* out, int64_t ldOut, float* part,
+                             hipStream_t s);
 
 hipError_t launch_sinkhorn(const float* mixes, int M, const float* scale, const float* base,
                            int iters, float pre_eps, float sk_eps, float post_mult, float* pre,

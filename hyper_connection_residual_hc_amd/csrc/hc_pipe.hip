@@ -1,0 +1,435 @@
+// Mix stats of a residual, alone or fused behind hc post (deepseek_v4.py,
+// DeepseekV4DecoderLayer.hc_pre's mix stats; DeepseekV4DecoderLayer.forward's fused
+// mhc_fused_post_pre, which takes the previous sublayer's hc post together with the next
+// hc pre). Per row x (flattened stream-major, 4H values) the kernel produces, for each of 8
+// column slices, the partial dots d[f] = sum_k fn[f, k] x_k (24 of them) and sum_k x_k^2.
+// In the fused form x is the bf16 R' = post * y + comb^T R that the kernel also stores.
+//
+// Arithmetic: the 24 x 4H projection runs on the matrix cores (v_mfma_f32_16x16x32_bf16).
+// x is exactly bf16; fn is fp32, split once per weight into three bf16 parts hi + mid + lo
+// (each the round-to-nearest-even of what the earlier parts leave). bf16 products are exact
+// in fp32 and the three parts carry fn to ~24 significant bits. The 72 (part, row) columns are
+// packed into 5 B-operand tiles of 16 feeding two accumulators; sum x^2 is the diagonal of the
+// 16x16 Gram tile of x with itself.
+//
+// Slices: slice s covers columns h in [s*H/8, (s+1)*H/8) of all four streams, so the fused
+// kernel produces every stream of R' for its columns. Block b takes slice b % 8: with
+// round-robin dispatch each XCD keeps one slice of packed fn (3.3 MB / 8) in its L2.
+//
+// Work layout (one persistent block of 8 waves per CU):
+//  * a tile is 64 rows; a stage is 64 columns of each stream (64 rows x 512 B);
+//  * waves 0-3 (producers) stream a stage with wave loads of 8 rows x 128 B (whole cache
+//    lines), compute R' in the fused form, store it, and write the bf16 stage into one slot of
+//    a two-slot LDS ring; their loads run four stages ahead;
+//  * waves 4-7 (consumers) multiply the previous stage: consumer q owns stream q (2 chunks of
+//    32 columns) for all 64 rows, so one fn operand load serves 64 rows;
+//  * one block barrier per stage. Producer and consumer waves keep separate in-order load
+//    counters, so waiting for fn operands never waits for HBM.
+// The LDS tile stores 16-byte unit u of row r at unit u ^ (r & 15): the consumers' 16-byte
+// reads of 16 rows hit 16 distinct bank groups.
+//
+// Partials go to a workspace [8][M][32] (24 dots, sum of squares); consumers sum their four
+// streams' accumulators in stream order. Nothing depends on M or on where a row sits in its
+// tile (rows past the end recompute row M-1 and store identical bits), so any row slice of a
+// call gives the same bits as the full call.
+#include "hc_launch.h"
+
+namespace hc {
+
+constexpr int kPipeH = 64;                         // columns of each stream per stage
+constexpr int kRowElems = kHC * kPipeH;            // 256 bf16 per row per stage (512 B)
+constexpr int kRowUnits = kRowElems / 8;           // 32 units of 16 B
+constexpr int kStageChunks = kRowElems / 32;       // 8 MFMA chunks per stage
+constexpr int kSlotElems = kStatsRows * kRowElems; // 16384 bf16 = 32 KB
+constexpr int kItemsPerLane = (kStatsRows * (kPipeH / 8)) / 256;  // 2 (row, 8-column) items
+constexpr int kEpiCols = 33;                       // 32 accumulator columns + sum of squares
+constexpr int kCoefs = kHC + kHC * kHC;            // post(4) + comb(16) per row
+
+// ---- fn packing -------------------------------------------------------------------------------
+// Packed index (8-element units): ((s*NCS + c)*5 + t)*64 + lane with NCS = 4*(H/8)/32 chunks
+// per slice. Chunk c of slice s is stage p = c / 8, stream j = (c % 8) / 2, half hq = c % 2: it
+// covers flattened columns k = j*H + s*(H/8) + 64p + 32hq + [0, 32). Lane (n = lane%16,
+// g = lane/16) of tile t holds the 8 columns k0 + 8g + [0..7] of the (part, fn row) the tile
+// assigns to n:
+//   t0: hi  of row n        t1: mid of row n        t2: lo of row n          (rows 0..15)
+//   t3: n < 8: hi of row 16+n;  n >= 8: mid of row 8+n                        (rows 16..23)
+//   t4: n < 8: lo of row 16+n;  n >= 8: zero
+// Tiles t0..t2 accumulate into one 16-column accumulator (column f = row f), tiles t3..t4 into
+// a second one whose column 16+n holds hi + lo of row 16+n and column 24+n its mid part.
+__device__ __forceinline__ float bf16_round(float v) { return (float)(__bf16)v; }
+
+__device__ __forceinline__ void pack_slot(int t, int n, int* row, int* part) {
+  if (t < 3) {
+    *row = n;
+    *part = t;
+  } else if (t == 3) {
+    *row = n < 8 ? 16 + n : 8 + n;
+    *part = n < 8 ? 0 : 1;
+  } else {
+    *row = n < 8 ? 16 + n : -1;
+    *part = 2;
+  }
+}
+
+__device__ __forceinline__ int64_t chunk_col0(int s, int c, int H) {
+  const int p = c >> 3, j = (c & 7) >> 1, hq = c & 1;
+  return (int64_t)j * H + (int64_t)s * (H / kSlices) + 64 * p + 32 * hq;
+}
+
+__global__ __launch_bounds__(256) void fn_pack_kernel(const float* __restrict__ fn, int H,
+                                                      uint16_t* __restrict__ out) {
+  const int NCS = (int)chunks_per_slice(H);
+  const int64_t total = (int64_t)kSlices * NCS * kPackTiles * 64;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int lane = (int)(gid & 63);
+  int64_t r = gid >> 6;
+  const int t = (int)(r % kPackTiles);
+  r /= kPackTiles;
+  const int c = (int)(r % NCS);
+  const int s = (int)(r / NCS);
+  int f, part;
+  pack_slot(t, lane & 15, &f, &part);
+  const int64_t k = chunk_col0(s, c, H) + 8 * (lane >> 4);
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float val = 0.0f;
+    if (f >= 0) {
+      const float a = fn[(int64_t)f * 4 * H + k + e];
+      const float hi = bf16_round(a);
+      const float r1 = a - hi;  // exact
+      const float mid = bf16_round(r1);
+      const float r2 = r1 - mid;  // exact
+      const float lo = bf16_round(r2);
+      val = part == 0 ? hi : (part == 1 ? mid : lo);
+    }
+    v[e] = val;
+  }
+  st16(out + gid * 8, pack8(v));  // the parts are exact bf16 values: packing does not round
+}
+
+hipError_t launch_fn_pack(const float* fn, int H, uint16_t* fn_packed, hipStream_t s) {
+  const int64_t total = (int64_t)kSlices * chunks_per_slice(H) * kPackTiles * 64;
+  hipLaunchKernelGGL(fn_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, fn,
+                     H, fn_packed);
+  return hipGetLastError();
+}
+
+// ---- the pipelined kernel ---------------------------------------------------------------------
+struct PipeArgs {
+  const uint16_t* x;  // fused form: the sublayer output [M, H]
+  int64_t ldX;
+  const uint16_t* R;  // residual [M, 4, H]
+  int64_t ldR;
+  const float* post;  // fused form: [M, 4]
+  const float* comb;  // fused form: [M, 4, 4]
+  const uint16_t* fnp;
+  uint16_t* out;      // fused form: R' [M, 4, H]
+  int64_t ldOut;
+  float* part;        // [8][M][32]
+  int M, H;
+  int tiles;          // ceil(M / 64)
+  int blocks_per_slice;
+};
+
+struct LdsLayout {
+  uint16_t ring[2][kSlotElems];                  // 64 KB
+  float epi[2][kHC][kStatsRows][kEpiCols];       // 66 KB
+  float coef[2][kStatsRows][kCoefs];             // 10 KB
+};
+
+__device__ __forceinline__ int swz(int row, int unit) { return unit ^ (row & 15); }
+
+template <bool kPost>
+__global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
+  __shared__ __attribute__((aligned(16))) LdsLayout L;
+
+  const int s = blockIdx.x % kSlices;
+  const int kb = blockIdx.x / kSlices;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int M = a.M, H = a.H;
+  const int nstage = (H / kSlices) / kPipeH;
+  const int my_tiles = kb < a.tiles ? (a.tiles - 1 - kb) / a.blocks_per_slice + 1 : 0;
+  const int total = my_tiles * nstage;
+  const int hs = s * (H / kSlices);
+  if (total == 0) return;  // block-uniform: no barrier is skipped by part of the block
+
+  auto tile_of = [&](int sigma) { return kb + (sigma / nstage) * a.blocks_per_slice; };
+
+  if (wave < 4) {
+    // ===================================== producers ======================================
+    // item it of this lane: row 16*wave + 8*it + lane/8, 8-column group lane%8
+    const int hg = lane & 7;
+    u32x4 ld0[kItemsPerLane][kHC + 1], ld1[kItemsPerLane][kHC + 1];
+    u32x4 ld2[kItemsPerLane][kHC + 1], ld3[kItemsPerLane][kHC + 1];
+    auto issue = [&](int sigma, u32x4 (&d)[kItemsPerLane][kHC + 1]) {
+      const int sg = min(sigma, total - 1);  // past the end: reload the last stage (unused)
+      const int T = tile_of(sg), p = sg - (sg / nstage) * nstage;
+      const int h = hs + 64 * p + 8 * hg;
+#pragma unroll
+      for (int it = 0; it < kItemsPerLane; ++it) {
+        const int row = min(T * kStatsRows + 16 * wave + 8 * it + (lane >> 3), M - 1);
+        const uint16_t* rr = a.R + (int64_t)row * a.ldR + h;
+#pragma unroll
+        for (int i = 0; i < kHC; ++i) d[it][i] = ld16_stream(rr + (int64_t)i * H);
+        if (kPost) d[it][kHC] = ld16_stream(a.x + (int64_t)row * a.ldX + h);
+      }
+    };
+    auto produce = [&](int sigma, u32x4 (&d)[kItemsPerLane][kHC + 1]) {
+      const int T = tile_of(sigma), p = sigma - (sigma / nstage) * nstage;
+      uint16_t* slot = L.ring[sigma & 1];
+#pragma unroll
+      for (int it = 0; it < kItemsPerLane; ++it) {
+        const int lrow = 16 * wave + 8 * it + (lane >> 3);
+        u32x4 st[kHC];
+        if (kPost) {
+          const int row = min(T * kStatsRows + lrow, M - 1);
+          const float* cf = L.coef[(sigma / nstage) & 1][lrow];
+          float pj[kHC], cij[kHC][kHC];
+#pragma unroll
+          for (int j = 0; j < kHC; ++j) pj[j] = cf[j];
+#pragma unroll
+          for (int i = 0; i < kHC; ++i)
+#pragma unroll
+            for (int j = 0; j < kHC; ++j) cij[i][j] = cf[kHC + i * kHC + j];
+          float xf[8], rf[kHC][8];
+          unpack8(d[it][kHC], xf);
+#pragma unroll
+          for (int i = 0; i < kHC; ++i) unpack8(d[it][i], rf[i]);
+          // same operation order as the standalone hc post kernel: identical bits
+#pragma unroll
+          for (int j = 0; j < kHC; ++j) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float acc = pj[j] * xf[e];
+#pragma unroll
+              for (int i = 0; i < kHC; ++i) acc = __fmaf_rn(cij[i][j], rf[i][e], acc);
+              o[e] = acc;
+            }
+            st[j] = pack8(o);
+          }
+          // rows past the end hold row M-1's inputs and coefficients: they store its bits again
+          uint16_t* orow = a.out + (int64_t)row * a.ldOut + hs + 64 * p + 8 * hg;
+#pragma unroll
+          for (int j = 0; j < kHC; ++j) st16(orow + (int64_t)j * H, st[j]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < kHC; ++i) st[i] = d[it][i];
+        }
+#pragma unroll
+        for (int j = 0; j < kHC; ++j)
+          *reinterpret_cast<u32x4*>(&slot[lrow * kRowElems + 8 * swz(lrow, 8 * j + hg)]) = st[j];
+      }
+    };
+
+    issue(0, ld0);
+    issue(1, ld1);
+    issue(2, ld2);
+    issue(3, ld3);
+    __syncthreads();  // the consumers' first coefficient tile is in LDS
+    // four iterations per trip so the four load buffers keep fixed registers; stage sigma's
+    // loads were issued four iterations earlier
+    for (int sigma = 0; sigma <= total; sigma += 4) {
+      if (sigma < total) {
+        produce(sigma, ld0);
+        issue(sigma + 4, ld0);
+      }
+      __syncthreads();
+      if (sigma + 1 > total) break;
+      if (sigma + 1 < total) {
+        produce(sigma + 1, ld1);
+        issue(sigma + 5, ld1);
+      }
+      __syncthreads();
+      if (sigma + 2 > total) break;
+      if (sigma + 2 < total) {
+        produce(sigma + 2, ld2);
+        issue(sigma + 6, ld2);
+      }
+      __syncthreads();
+      if (sigma + 3 > total) break;
+      if (sigma + 3 < total) {
+        produce(sigma + 3, ld3);
+        issue(sigma + 7, ld3);
+      }
+      __syncthreads();
+    }
+  } else {
+    // ===================================== consumers ======================================
+    const int q = wave - 4;  // stream
+    const int r16 = lane & 15, g = lane >> 4;
+    const u32x4* bslice = reinterpret_cast<const u32x4*>(a.fnp) + (int64_t)s * chunks_per_slice(H) * kPackTiles * 64 + lane;
+    f32x4 d0[4], d1[4], sq[4];
+    auto zero_acc = [&]() {
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        d0[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+        d1[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sq[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+    // post / comb of tile T's 64 rows into coefficient slot T & 1 (fused form)
+    auto load_coef = [&](int tile_iter) {
+      const int T = kb + tile_iter * a.blocks_per_slice;
+      float* dst = &L.coef[tile_iter & 1][0][0];
+      for (int v = threadIdx.x - 256; v < kStatsRows * 5; v += 256) {
+        const int lr = v / 5, k = v - lr * 5;
+        const int row = min(T * kStatsRows + lr, M - 1);
+        const float* src = k == 0 ? a.post + (int64_t)row * kHC : a.comb + (int64_t)row * 16 + 4 * (k - 1);
+        *reinterpret_cast<f32x4*>(dst + lr * kCoefs + 4 * k) = *reinterpret_cast<const f32x4*>(src);
+      }
+    };
+    // partials of tile T from epilogue slot T & 1
+    auto flush = [&](int tile_iter) {
+      const int T = kb + tile_iter * a.blocks_per_slice;
+      const auto& ep = L.epi[tile_iter & 1];
+      for (int idx = threadIdx.x - 256; idx < kStatsRows * (kMix + 1); idx += 256) {
+        const int row = idx / (kMix + 1);
+        const int f = idx - row * (kMix + 1);
+        const int grow = T * kStatsRows + row;
+        if (grow >= M) continue;
+        float v = 0.0f;
+        if (f < 16) {
+#pragma unroll
+          for (int w = 0; w < kHC; ++w) v += ep[w][row][f];
+        } else if (f < kMix) {
+#pragma unroll
+          for (int w = 0; w < kHC; ++w) v += ep[w][row][f] + ep[w][row][f + 8];
+        } else {
+#pragma unroll
+          for (int w = 0; w < kHC; ++w) v += ep[w][row][32];
+        }
+        a.part[((int64_t)s * M + grow) * kPartStride + f] = v;
+      }
+    };
+
+    // fn operands of stage k (clamped to the last stage, so the prefetch past the end reloads
+    // valid memory) for this consumer's two chunks
+    auto load_b = [&](int k, u32x4 (&b)[2][kPackTiles]) {
+      const int kk = min(k, total - 1);
+      const int p = kk - (kk / nstage) * nstage;
+#pragma unroll
+      for (int hq = 0; hq < 2; ++hq)
+#pragma unroll
+        for (int t = 0; t < kPackTiles; ++t)
+          b[hq][t] = bslice[((int64_t)(p * kStageChunks + 2 * q + hq) * kPackTiles + t) * 64];
+    };
+    // iteration sigma: the next tile's coefficients (fused form), the previous tile's partials,
+    // the prefetch of stage sigma's fn operands, then stage sigma - 1's MFMAs
+    auto step = [&](int sigma, u32x4 (&bnext)[2][kPackTiles], const u32x4 (&bcur)[2][kPackTiles]) {
+      const int prev = sigma - 1;
+      if (kPost && sigma < total && (sigma + 1) % nstage == 0 && (sigma + 1) / nstage < my_tiles)
+        load_coef((sigma + 1) / nstage);  // used by the producers from sigma + 1
+      if (prev >= nstage && prev % nstage == 0) flush(prev / nstage - 1);
+      load_b(sigma, bnext);
+      if (prev >= 0) {
+        const int p = prev - (prev / nstage) * nstage;
+        const uint16_t* slot = L.ring[prev & 1];
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub) {
+            const int row = 16 * sub + r16;
+            const u32x4 av = *reinterpret_cast<const u32x4*>(&slot[row * kRowElems + 8 * swz(row, 8 * q + 4 * hq + g)]);
+            const bf16x8 xa = __builtin_bit_cast(bf16x8, av);
+            d0[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, bcur[hq][0]), d0[sub], 0, 0, 0);
+            d1[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, bcur[hq][3]), d1[sub], 0, 0, 0);
+            sq[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, xa, sq[sub], 0, 0, 0);
+            d0[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, bcur[hq][1]), d0[sub], 0, 0, 0);
+            d1[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, bcur[hq][4]), d1[sub], 0, 0, 0);
+            d0[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, bcur[hq][2]), d0[sub], 0, 0, 0);
+          }
+        }
+        if (p == nstage - 1) {
+          // tile done: accumulators into its epilogue slot (16x16 layout: lane holds rows
+          // 4*(lane/16) + i of column lane % 16), flushed in the iteration after the barrier
+          auto& ep = L.epi[(prev / nstage) & 1][q];
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = sub * 16 + 4 * g + i;
+              ep[row][r16] = d0[sub][i];
+              ep[row][16 + r16] = d1[sub][i];
+              if (r16 == 4 * g + i) ep[sub * 16 + r16][32] = sq[sub][i];
+            }
+          }
+          zero_acc();
+        }
+      }
+      __syncthreads();
+    };
+
+    zero_acc();
+    if (kPost) load_coef(0);
+    __syncthreads();  // matches the producers' prologue barrier
+    // stage k's operands live in buffer k % 2; two iterations per trip keep fixed registers
+    u32x4 b0[2][kPackTiles], b1[2][kPackTiles];
+    for (int sigma = 0; sigma <= total; sigma += 2) {
+      step(sigma, b0, b1);
+      if (sigma + 1 > total) break;
+      step(sigma + 1, b1, b0);
+    }
+    flush(my_tiles - 1);
+  }
+}
+
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+static hipError_t launch_pipe(bool fused, PipeArgs args, hipStream_t s) {
+  args.tiles = (args.M + kStatsRows - 1) / kStatsRows;
+  args.blocks_per_slice = max(1, min(args.tiles, device_cus() / kSlices));
+  const dim3 grid((unsigned)(args.blocks_per_slice * kSlices)), block(512);
+  if (fused)
+    hipLaunchKernelGGL(pipe_kernel<true>, grid, block, 0, s, args);
+  else
+    hipLaunchKernelGGL(pipe_kernel<false>, grid, block, 0, s, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, int M, int H,
+                        float* part, hipStream_t s) {
+  PipeArgs args{};
+  args.R = R;
+  args.ldR = ldR;
+  args.fnp = fn_packed;
+  args.part = part;
+  args.M = M;
+  args.H = H;
+  return launch_pipe(false, args, s);
+}
+
+hipError_t launch_post_stats(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                             const float* post, const float* comb, const uint16_t* fn_packed,
+                             int M, int H, uint16_t* out, int64_t ldOut, float* part,
+                             hipStream_t s) {
+  PipeArgs args{};
+  args.x = x;
+  args.ldX = ldX;
+  args.R = R;
+  args.ldR = ldR;
+  args.post = post;
+  args.comb = comb;
+  args.fnp = fn_packed;
+  args.out = out;
+  args.ldOut = ldOut;
+  args.part = part;
+  args.M = M;
+  args.H = H;
+  return launch_pipe(true, args, s);
+}
+
+}  // namespace hc

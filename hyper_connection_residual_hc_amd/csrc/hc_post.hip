@@ -5,7 +5,9 @@
 // Pure streaming: per row 10 KB of x and 40 KB of R in, 40 KB of Rout out. One wavefront
 // owns one row and 512 consecutive columns; each lane moves 8 columns of x and of all four
 // streams with 16-byte accesses, so every wave-wide access is a contiguous 1 KB. The row's
-// 20 coefficients are wave-uniform and come in through scalar loads.
+// 20 coefficients are wave-uniform and come in through scalar loads. x and R are read once
+// (non-temporal loads); Rout is stored through the caches, since the next hc pre reads it
+// right away and it fits the Infinity Cache at prefill sizes.
 #include "hc_launch.h"
 
 namespace hc {
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(256) void post_kernel(const uint16_t* __restrict__ 
       for (int i = 0; i < kHC; ++i) a = __fmaf_rn(cij[i][j], rf[i][e], a);
       o[e] = a;
     }
-    st16_stream(orow + (int64_t)j * H, pack8(o));
+    st16(orow + (int64_t)j * H, pack8(o));
   }
 }
 

@@ -219,3 +219,49 @@ def pre(R: torch.Tensor, fn_packed: torch.Tensor, scale: torch.Tensor, base: tor
               post_mult, norm_eps, y.data_ptr(), _rows(y, H), _ptr(pre_), post_.data_ptr(),
               comb.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(R))
     return y, post_, comb, pre_
+
+
+# ---- fused post -> pre -----------------------------------------------------------------------
+def post_pre_workspace_bytes(M: int, H: int) -> int:
+    return int(_lib.lib().hc_post_pre_workspace_bytes(M, H))
+
+
+def post_pre(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.Tensor,
+             fn_packed: torch.Tensor, scale: torch.Tensor, base: torch.Tensor,
+             weight: torch.Tensor, rms_eps: float = RMS_EPS, pre_eps: float = HC_EPS,
+             sinkhorn_eps: float = HC_EPS, iters: int = ITERS, post_mult: float = POST_MULT,
+             norm_eps: float = RMS_EPS, want_pre: bool = False, out=None,
+             workspace: Optional[torch.Tensor] = None):
+    """hc post of one site fused with hc pre of the next:
+    (R' [M, 4, H], y [M, H], post' [M, 4], comb' [M, 4, 4], pre' [M, 4] or None)."""
+    M, H, ldR = _residual(R)
+    _need(x, "x", torch.bfloat16, 2)
+    if tuple(x.shape) != (M, H):
+        raise ValueError(f"x must be [{M}, {H}]")
+    _contig(post_, "post", torch.float32, (M, HC))
+    _contig(comb, "comb", torch.float32, (M, HC, HC))
+    _contig(scale, "scale", torch.float32, (3,))
+    _contig(base, "base", torch.float32, (MIX,))
+    _contig(weight, "weight", torch.bfloat16, (H,))
+    dev = R.device
+    if out is None:
+        out = (torch.empty(M, HC, H, dtype=torch.bfloat16, device=dev),
+               torch.empty(M, H, dtype=torch.bfloat16, device=dev),
+               torch.empty(M, HC, dtype=torch.float32, device=dev),
+               torch.empty(M, HC, HC, dtype=torch.float32, device=dev),
+               torch.empty(M, HC, dtype=torch.float32, device=dev) if want_pre else None)
+    Rn, y, post_o, comb_o, pre_o = out
+    _, _, ldOut = _residual(Rn)
+    _need(y, "y", torch.bfloat16, 2)
+    _contig(post_o, "post_out", torch.float32, (M, HC))
+    _contig(comb_o, "comb_out", torch.float32, (M, HC, HC))
+    if pre_o is not None:
+        _contig(pre_o, "pre_out", torch.float32, (M, HC))
+    ws = _workspace(post_pre_workspace_bytes(M, H), dev, workspace)
+    _lib.call("hc_post_pre", x.data_ptr(), _rows(x, H), R.data_ptr(), ldR, post_.data_ptr(),
+              comb.data_ptr(), fn_packed.data_ptr(), scale.data_ptr(), base.data_ptr(),
+              weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult,
+              norm_eps, Rn.data_ptr(), ldOut, y.data_ptr(), _rows(y, H), _ptr(pre_o),
+              post_o.data_ptr(), comb_o.data_ptr(), ws.data_ptr(),
+              ws.numel() * ws.element_size(), _stream(R))
+    return Rn, y, post_o, comb_o, pre_o

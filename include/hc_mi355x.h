@@ -68,7 +68,7 @@ HC_API int hc_abi_version(void);
  *
  * fn:        fp32 [24, 4H] row-major (device).
  * fn_packed: hc_fn_packed_bytes(H) bytes (device, 16-byte aligned), written.
- * H:         multiple of 512.
+ * H:         multiple of 1024.
  * ------------------------------------------------------------------------------------- */
 HC_API size_t hc_fn_packed_bytes(int32_t H);
 HC_API int hc_fn_pack(const float* fn, int32_t H, uint16_t* fn_packed, void* stream);
@@ -84,7 +84,7 @@ HC_API int hc_fn_pack(const float* fn, int32_t H, uint16_t* fn_packed, void* str
  * sumsq:      fp32 [M] or NULL, written when given.
  * workspace:  >= hc_pre_stats_workspace_bytes(M, H) bytes of device memory, 256-byte aligned;
  *             its contents on entry do not matter.
- * H:          multiple of 512.
+ * H:          multiple of 1024.
  * ------------------------------------------------------------------------------------- */
 HC_API size_t hc_pre_stats_workspace_bytes(int64_t M, int32_t H);
 HC_API int hc_pre_stats(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, int64_t M,
@@ -157,7 +157,7 @@ HC_API int mxfp8_quant_rows(const uint16_t* y, int64_t ldY, int64_t M, int32_t K
  * hc_pre_stats -> hc_sinkhorn -> hc_combine_norm.
  *
  * pre may be NULL (not written); post fp32 [M, 4], comb fp32 [M, 4, 4], y bf16 [M, H] (ldY).
- * H: as hc_combine_norm (every such H is a multiple of 512). workspace: >= hc_pre_workspace_bytes(M, H).
+ * H: as hc_combine_norm and a multiple of 1024. workspace: >= hc_pre_workspace_bytes(M, H).
  * ------------------------------------------------------------------------------------- */
 HC_API size_t hc_pre_workspace_bytes(int64_t M, int32_t H);
 HC_API int hc_pre(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed,
@@ -166,6 +166,32 @@ HC_API int hc_pre(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed,
                   int32_t iters, float post_mult, float norm_eps,
                   uint16_t* y, int64_t ldY, float* pre, float* post, float* comb,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Fused hc post -> hc pre across a sublayer boundary (deepseek_v4.py,
+ * DeepseekV4DecoderLayer.forward: mhc_fused_post_pre takes the residual, the previous
+ * site's post / comb and the sublayer output together with the next site's fn, scale, base and
+ * norm weight, and returns the new residual, the next post / comb and the normalised input).
+ *   Rout = hc_post(x, R, post, comb)                      (bit-identical to hc_post)
+ *   (y, pre_out, post_out, comb_out) = hc_pre(Rout, ...)  (bit-identical to hc_pre on Rout)
+ * The post kernel also computes the mix stats of the bf16 Rout it writes, so Rout is read
+ * back once (by the combine) instead of twice.
+ *
+ * x: bf16 [M, H] (ldX); R: bf16 [M, 4, H] (ldR); post fp32 [M, 4], comb fp32 [M, 4, 4],
+ * contiguous and 16-byte aligned; fn_packed / scale / base / weight: the next site's, as
+ * for hc_pre. Rout: bf16 [M, 4, H] (ldOut); y: bf16 [M, H] (ldY); pre_out (or NULL),
+ * post_out fp32 [M, 4], comb_out fp32 [M, 4, 4]: written. H: as hc_pre.
+ * workspace: >= hc_post_pre_workspace_bytes(M, H). Outputs must not overlap any input.
+ * ------------------------------------------------------------------------------------- */
+HC_API size_t hc_post_pre_workspace_bytes(int64_t M, int32_t H);
+HC_API int hc_post_pre(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                       const float* post, const float* comb, const uint16_t* fn_packed,
+                       const float* scale, const float* base, const uint16_t* weight,
+                       int64_t M, int32_t H, float rms_eps, float pre_eps, float sinkhorn_eps,
+                       int32_t iters, float post_mult, float norm_eps,
+                       uint16_t* Rout, int64_t ldOut, uint16_t* y, int64_t ldY, float* pre_out,
+                       float* post_out, float* comb_out, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -43,8 +43,8 @@ def test_status_strings(L):
 
 def test_sizes(L):
     H = 5120
-    assert L.hc_fn_packed_bytes(H) == 8 * (H // 64) * 5 * 64 * 8 * 2
-    assert L.hc_fn_packed_bytes(256) == 0  # stats need a multiple of 512
+    assert L.hc_fn_packed_bytes(H) == 8 * (4 * (H // 8) // 32) * 5 * 64 * 8 * 2
+    assert L.hc_fn_packed_bytes(512) == 0  # stats need a multiple of 1024
     assert L.hc_fn_packed_bytes(100) == 0
     assert L.hc_pre_stats_workspace_bytes(4096, H) == 8 * 4096 * 32 * 4
     assert L.hc_pre_workspace_bytes(0, H) == 0

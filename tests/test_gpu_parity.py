@@ -41,12 +41,17 @@ def test_fn_pack_reconstructs_fn(attn):
     appears exactly once, the padding is zero, and the parts decrease in magnitude."""
     gu.say("fn_pack H=5120 seed=11")
     p = o.bf16_to_f64(attn.fnp.cpu().numpy().view(np.uint16))
-    NCS = gu.H // 64  # 32-column chunks per slice of 4H/8 flattened columns
-    p = p.reshape(8, NCS, 5, 4, 16, 8)  # s, c, t, g, n, e
+    S = 8  # column slices
+    NCS = 4 * (gu.H // S) // 32  # 32-column chunks per slice
+    p = p.reshape(S, NCS, 5, 4, 16, 8)  # s, c, t, g, n, e
     fn = attn.fn.numpy().astype(np.float64)
     parts = np.zeros((3,) + fn.shape)
-    k_idx = (np.arange(8)[:, None, None, None] * (gu.H // 2)
-             + 32 * np.arange(NCS)[None, :, None, None]
+    # chunk c of slice s: stage c // 8, stream (c % 8) // 2, half c % 2 -> columns
+    # stream*H + s*H/8 + 64*stage + 32*half + 8g + e
+    c = np.arange(NCS)
+    col0 = ((c % 8) // 2) * gu.H + 64 * (c // 8) + 32 * (c % 2)
+    k_idx = (np.arange(S)[:, None, None, None] * (gu.H // S)
+             + col0[None, :, None, None]
              + 8 * np.arange(4)[None, None, :, None]
              + np.arange(8)[None, None, None, :]).reshape(-1)
     seen = set()
@@ -236,3 +241,53 @@ def test_small_hidden_size():
     out = ops.post(gu.dev(x), gu.dev(R), gu.dev(post32), gu.dev(comb32))
     oR, _ = o.hc_post(inputs.bits(x), inputs.bits(R), post32.numpy(), comb32.numpy())
     gu.assert_bf16_close(gu.bits_of(out), oR, "R'")
+
+
+# ------------------------------------------------------------------------------------------
+# fused post -> pre (hc_post_pre)
+# ------------------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def ffn():
+    return gu.Site(inputs.SEED_FFN, inputs.SEED_NORM_FFN)
+
+
+@pytest.mark.parametrize("M", [1, 63, 65, 300, 2112, 4096])
+def test_fused_post_pre_equals_post_then_pre(attn, ffn, M):
+    """hc_post_pre gives the bits of hc_post followed by hc_pre on its output. M covers one
+    partial tile, tile edges, fewer tiles than blocks, and more tiles than blocks (2112 rows =
+    33 tiles: one block per slice takes two tiles, the others one)."""
+    gu.say(f"hc_post_pre fused M={M}")
+    R = gu.dev(inputs.residual(M, M + 5))
+    x = gu.dev(inputs.sublayer_out(M, M + 6))
+    _, post, comb, _ = ops.pre(R, attn.fnp, attn.scale_d, attn.base_d, attn.w_d)
+    Rn, y, post2, comb2, pre2 = ops.post_pre(
+        x, R, post, comb, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d, want_pre=True,
+        out=(_poison_bf16(M, 4, gu.H), _poison_bf16(M, gu.H), _poison_f32(M, 4),
+             _poison_f32(M, 4, 4), _poison_f32(M, 4)))
+    Rn_ref = ops.post(x, R, post, comb)
+    y_ref, post_ref, comb_ref, pre_ref = ops.pre(Rn_ref, ffn.fnp, ffn.scale_d, ffn.base_d,
+                                                 ffn.w_d, want_pre=True)
+    assert torch.equal(Rn.view(torch.int16), Rn_ref.view(torch.int16))
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    assert torch.equal(post2, post_ref) and torch.equal(comb2, comb_ref) and torch.equal(pre2, pre_ref)
+
+
+def test_fused_post_pre_matches_oracle(attn, ffn):
+    """Config 3 (M = 1500) through the fused op, against the oracle's own chain."""
+    M = 1500
+    gu.say(f"hc_post_pre vs oracle M={M}")
+    R = inputs.residual(M, M)
+    x = inputs.sublayer_out(M, M + 1)
+    ref1 = attn.oracle_pre(inputs.bits(R))
+    post32 = torch.from_numpy(ref1["post"].astype(np.float32))
+    comb32 = torch.from_numpy(ref1["comb"].astype(np.float32))
+    Rn, y, post2, comb2, pre2 = ops.post_pre(gu.dev(x), gu.dev(R), gu.dev(post32), gu.dev(comb32),
+                                             ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d,
+                                             want_pre=True)
+    oR1, oR1_bits = o.hc_post(inputs.bits(x), inputs.bits(R), post32.numpy(), comb32.numpy())
+    ref2 = ffn.oracle_pre(oR1_bits)
+    gu.assert_bf16_close(gu.bits_of(Rn), oR1, "R'")
+    gu.assert_bf16_close(gu.bits_of(y), ref2["y"], "y ffn")
+    for name, g in (("pre", pre2), ("post", post2), ("comb", comb2)):
+        err = np.abs(gu.f32_np(g) - ref2[name]).max()
+        assert err <= 2e-3, f"{name} ffn (chain): {err}"

@@ -42,6 +42,8 @@ def test_row_slices_are_bit_identical(attn, M, W):
     full["combine"] = (ops.combine_norm(R, pre, attn.w_d),)
     full["post"] = (ops.post(x, R, post, comb),)
     full["mxfp8"] = ops.mxfp8_quant_rows(y)
+    full["post_pre"] = ops.post_pre(x, R, post, comb, attn.fnp, attn.scale_d, attn.base_d,
+                                    attn.w_d, want_pre=True)
 
     def run(lo, hi):
         sl = slice(lo, hi)
@@ -52,6 +54,8 @@ def test_row_slices_are_bit_identical(attn, M, W):
             "combine": (ops.combine_norm(R[sl], pre[sl], attn.w_d),),
             "post": (ops.post(x[sl], R[sl], post[sl], comb[sl]),),
             "mxfp8": ops.mxfp8_quant_rows(y[sl]),
+            "post_pre": ops.post_pre(x[sl], R[sl], post[sl], comb[sl], attn.fnp, attn.scale_d,
+                                     attn.base_d, attn.w_d, want_pre=True),
         }
 
     shards = [(r * M // W, (r + 1) * M // W) for r in range(W)]
