@@ -8,15 +8,25 @@ at setup. Inputs are seeded synthetic tensors with the distributions of the one-
 several independent input sets rotate so that no step finds its inputs in the 256 MB
 Infinity Cache.
 
+The default path runs the step as the fused post -> pre in its two calls: hc_post_stats (R'
+and the FFN site's mix-stat partials in one pass: the dominant kernel) and hc_pre_finish.
+--path unfused runs hc_post then hc_pre.
+
 Prints one JSON line: rows/s of the whole step, the HBM roofline of the dominant kernel
-(hc_post, timed live with HIP events on the stream it runs on) and the CPU oracle's rows/s
-on a bounded sample of the same workload.
+(timed live with HIP events recorded on the stream it runs on, around each launch) and the
+CPU oracle's rows/s on a bounded sample of the same workload. The roofline's "traffic" is the
+HBM byte count that rocprofv3's FETCH_SIZE / WRITE_SIZE counters gave for that kernel; it is
+read from the summary under profiles/ and reported only while the kernel's source files
+still hash to what that summary records (null otherwise).
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,8 +41,39 @@ PEAK_HBM_GBS = 8000.0
 # algorithmic bytes per row (what the method must move at least once)
 POST_BYTES_ROW = 2 * (HC * H + H + HC * H) + 4 * (HC + HC * HC)  # R + x in, R' out, post + comb
 PRE_BYTES_ROW = 2 * (HC * H + H) + 4 * (HC + HC + HC * HC)  # R in, y out, pre/post/comb out
-PRE_BYTES_CALL = 24 * 4 * H * 4 + 2 * H  # fn (fp32 layout) and the norm weight, once per call
+FN_BYTES = 24 * 4 * H * 4  # fn once per call (fp32 layout; the packed bf16 parts cost 1.25x)
+PRE_BYTES_CALL = FN_BYTES + 2 * H  # fn and the norm weight, once per call
 STEP_BYTES = M_BENCH * (POST_BYTES_ROW + PRE_BYTES_ROW) + PRE_BYTES_CALL
+# the dominant kernel of each path and the algorithmic bytes one launch moves
+ROOFLINE_KERNEL = {
+    "fused": ("pipe_kernel<true> (hc_post_stats)", M_BENCH * POST_BYTES_ROW + FN_BYTES,
+              ["hc_pipe.hip", "hc_device.h", "hc_launch.h"]),
+    "unfused": ("post_kernel (hc_post)", M_BENCH * POST_BYTES_ROW,
+                ["hc_post.hip", "hc_device.h", "hc_launch.h"]),
+}
+
+
+def kernel_source_hash(files) -> str:
+    csrc = os.path.join(ROOT, "hyper_connection_residual_hc_amd", "csrc")
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str, files):
+    """HBM bytes per launch of `kernel` from a profiles/ summary line
+    `traffic-record: kernel=<name> M=4096 source=<hash> bytes=<n>`, if its hash is current."""
+    want = kernel_source_hash(files)
+    pat = re.compile(r"traffic-record: kernel=(\S+) M=(\d+) source=(\w+) bytes=(\d+)")
+    name = kernel.split()[0]
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as fh:
+            for m in pat.finditer(fh.read()):
+                if m.group(1) == name and int(m.group(2)) == M_BENCH and m.group(3) == want:
+                    return int(m.group(4))
+    return None
 
 
 def cpu_baseline(rows: int, target_s: float):
@@ -119,10 +160,12 @@ def main() -> int:
         if ev is not None:
             ev[0].record()
         if args.path == "fused":
-            ops.post_pre(x, R, post, comb, fnp_f, sc_f, ba_f, w_f,
-                         out=(o["R1"], o["y"], o["post"], o["comb"], None), workspace=o["ws"])
+            # hc_post_pre as its two calls, so that the events can bracket the first kernel
+            ops.post_stats(x, R, post, comb, fnp_f, out=o["R1"], workspace=o["ws"])
             if ev is not None:
                 ev[1].record()
+            ops.pre_finish(o["R1"], o["ws"], sc_f, ba_f, w_f,
+                           out=(o["y"], o["post"], o["comb"], None))
         else:
             ops.post(x, R, post, comb, out=o["R1"])
             if ev is not None:
@@ -144,8 +187,8 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    post_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    pre_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    first_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    second_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
 
     # practical HBM ceiling for context: a plain 1 GiB device copy
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -161,9 +204,14 @@ def main() -> int:
     copy_gbs = 2 * src.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    post_bytes = M * POST_BYTES_ROW
-    post_gbs = post_bytes / (post_ms * 1e-3) / 1e9
-    pre_bytes = M * PRE_BYTES_ROW + PRE_BYTES_CALL
+    kname, kbytes, kfiles = ROOFLINE_KERNEL[args.path]
+    k_gbs = kbytes / (first_ms * 1e-3) / 1e9
+    if args.path == "fused":
+        kernels_ms = {"hc_post_stats (pipe_kernel<true>)": first_ms,
+                      "hc_pre_finish (pre_finish_kernel)": second_ms}
+    else:
+        kernels_ms = {"hc_post (post_kernel)": first_ms,
+                      "hc_pre (pipe_kernel<false> + pre_finish_kernel)": second_ms}
     rows_s = M / (ms_step * 1e-3)
     step_gbs = STEP_BYTES / (ms_step * 1e-3) / 1e9
     result = {
@@ -189,16 +237,18 @@ def main() -> int:
         "hbm_frac_step": step_gbs / PEAK_HBM_GBS,
         "algorithmic_bytes_step": STEP_BYTES,
         "copy_ceiling_gbps": copy_gbs,
-        "kernels_ms": {"hc_post": post_ms, "hc_pre (stats + finish)": pre_ms},
-        "pre_gbps": pre_bytes / (pre_ms * 1e-3) / 1e9,
+        "path": args.path,
+        "kernels_ms": kernels_ms,
         "roofline": {
-            "kernel": "hc_post (post_kernel)",
+            "kernel": kname,
             "bound": "hbm",
-            "achieved": post_gbs,
+            "achieved": k_gbs,
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": post_gbs / PEAK_HBM_GBS,
-            "traffic": None,
+            "frac": k_gbs / PEAK_HBM_GBS,
+            "algorithmic_bytes": kbytes,
+            "traffic": recorded_traffic(kname, kfiles),
+            "source": kernel_source_hash(kfiles),
         },
     }
     if not args.no_cpu_baseline:

@@ -318,4 +318,77 @@ HC_API int hc_post_pre(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_
                                         pre_out, post_out, comb_out, s));
 }
 
+
+// ---- the two halves of hc_post_pre ---------------------------------------------------------
+HC_API int hc_post_stats(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                         const float* post, const float* comb, const uint16_t* fn_packed,
+                         int64_t M, int32_t H, uint16_t* Rout, int64_t ldOut, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if (!stats_h_ok(H) || !hc::combine_h_supported(H) || !post_h_ok(H)) return HC_ERR_SHAPE;
+  if (M == 0) return HC_OK;
+  if (!x || !R || !post || !comb || !fn_packed || !Rout) return HC_ERR_NULL;
+  if ((st = check_residual(R, ldR, H))) return st;
+  if (ldX < H || ldOut < (int64_t)kHC * H) return HC_ERR_SHAPE;
+  if (!al16(x) || !al16(Rout) || !al16(post) || !al16(comb) || !al16(fn_packed) ||
+      (ldX * 2) % 16 || (ldOut * 2) % 16)
+    return HC_ERR_ALIGN;
+  if (!workspace || workspace_bytes < hc::stats_workspace_bytes(M)) return HC_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return HC_ERR_ALIGN;
+  const Span ins[5] = {rows_span(x, M, ldX, H, 2), rows_span(R, M, ldR, (int64_t)kHC * H, 2),
+                       rows_span(post, M, kHC, kHC, 4),
+                       rows_span(comb, M, kHC * kHC, kHC * kHC, 4),
+                       Span{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)}};
+  const Span outs[2] = {rows_span(Rout, M, ldOut, (int64_t)kHC * H, 2),
+                        Span{(uintptr_t)workspace, (uintptr_t)workspace + hc::stats_workspace_bytes(M)}};
+  if (overlaps(outs[0], outs[1])) return HC_ERR_ALIAS;
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 5; ++j)
+      if (overlaps(outs[i], ins[j])) return HC_ERR_ALIAS;
+  return launched(hc::launch_post_stats(x, ldX, R, ldR, post, comb, fn_packed, (int)M, H, Rout,
+                                        ldOut, static_cast<float*>(workspace), as_stream(stream)));
+}
+
+HC_API int hc_pre_finish(const uint16_t* R, int64_t ldR, const float* scale, const float* base,
+                         const uint16_t* weight, int64_t M, int32_t H, float rms_eps,
+                         float pre_eps, float sinkhorn_eps, int32_t iters, float post_mult,
+                         float norm_eps, uint16_t* y, int64_t ldY, float* pre, float* post,
+                         float* comb, const void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if (!stats_h_ok(H) || !hc::combine_h_supported(H)) return HC_ERR_SHAPE;
+  if (iters < 1 || iters > 100000) return HC_ERR_SHAPE;
+  if (!finite_nonneg(rms_eps) || !finite_nonneg(pre_eps) || !finite_nonneg(sinkhorn_eps) ||
+      !finite_nonneg(norm_eps) || !isfinite(post_mult))
+    return HC_ERR_ARG;
+  if (M == 0) return HC_OK;
+  if (!R || !scale || !base || !weight || !y || !post || !comb) return HC_ERR_NULL;
+  if ((st = check_residual(R, ldR, H))) return st;
+  if (ldY < H) return HC_ERR_SHAPE;
+  if (!al16(weight) || !al16(y) || (ldY * 2) % 16) return HC_ERR_ALIGN;
+  if (!workspace || workspace_bytes < hc::stats_workspace_bytes(M)) return HC_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return HC_ERR_ALIGN;
+  const Span ins[5] = {rows_span(R, M, ldR, (int64_t)kHC * H, 2),
+                       Span{(uintptr_t)scale, (uintptr_t)scale + 12},
+                       Span{(uintptr_t)base, (uintptr_t)base + kMix * 4},
+                       Span{(uintptr_t)weight, (uintptr_t)weight + (uintptr_t)H * 2},
+                       Span{(uintptr_t)workspace, (uintptr_t)workspace + hc::stats_workspace_bytes(M)}};
+  const Span outs[4] = {rows_span(y, M, ldY, H, 2), rows_span(post, M, kHC, kHC, 4),
+                        rows_span(comb, M, kHC * kHC, kHC * kHC, 4),
+                        pre ? rows_span(pre, M, kHC, kHC, 4) : Span{0, 0}};
+  for (int i = 0; i < 4; ++i) {
+    if (outs[i].b == outs[i].e) continue;
+    for (int j = 0; j < 5; ++j)
+      if (overlaps(outs[i], ins[j])) return HC_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (outs[j].b != outs[j].e && overlaps(outs[i], outs[j])) return HC_ERR_ALIAS;
+  }
+  return launched(hc::launch_pre_finish(static_cast<const float*>(workspace), R, ldR, scale, base,
+                                        weight, (int)M, H, rms_eps, pre_eps, sinkhorn_eps, iters,
+                                        post_mult, norm_eps, y, ldY, pre, post, comb,
+                                        as_stream(stream)));
+}
+
 }  // extern "C"

@@ -72,12 +72,10 @@ __device__ __forceinline__ float dpp(float v) {
 constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]: lane l reads lane l^1
 constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]: lane l reads lane l^2
 
-// lane l reads lane l^XOR (XOR < 32), through ds_swizzle's bit mode (no LDS memory access)
-template <int XOR>
-__device__ __forceinline__ float swz_xor(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
-                                                               0x1F | (XOR << 10)));
-}
+// row_ror:N (N = 4k): within each 16-lane row, lane l reads lane (l - N) mod 16
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+constexpr int kRowRor12 = 0x12C;
 
 // Sum over the 4 lanes of a quad (lanes 4q..4q+3).
 __device__ __forceinline__ float quad_sum(float v) {
@@ -90,12 +88,17 @@ __device__ __forceinline__ float quad_max(float v) {
   v = fmaxf(v, dpp<kQuadSwap2>(v));
   return v;
 }
-// Sum over the lanes {e, e^4, e^8, e^12} of each 16-lane group. Butterfly order, so every
-// lane of the group gets the identical sum.
+// Sum over the lanes {e, e+4, e+8, e+12} (mod 16) of each 16-lane group, lane e holding row
+// i = e / 4 of its column. Every lane forms ((v0 + v1) + (v2 + v3)) over the column's rows
+// (up to the order of the operands of each add, which does not change a rounded sum), so the
+// four lanes of a column get identical bits. With A = v + v[e-4]: an odd row holds the pair
+// (i, i-1) in A and finds the other pair two rows away; an even row reads both pairs from
+// its neighbours. DPP only: no LDS round trip.
 __device__ __forceinline__ float stride4_sum(float v) {
-  v += swz_xor<4>(v);
-  v += swz_xor<8>(v);
-  return v;
+  const float A = v + dpp<kRowRor4>(v);
+  const float odd = A + dpp<kRowRor8>(A);
+  const float even = dpp<kRowRor12>(A) + dpp<kRowRor4>(A);
+  return ((__lane_id() >> 2) & 1) ? odd : even;
 }
 
 // Sum over the whole wavefront, in a fixed order (every lane gets the same value).

@@ -23,11 +23,21 @@ inline size_t stats_workspace_bytes(int64_t M) { return (size_t)kSlices * (size_
 
 // Sum of one field of a row's slice partials, in slice order. Used by every consumer
 // of the partials, so the standalone and the fused pre give identical bits.
-__device__ __forceinline__ float slice_sum(const float* __restrict__ part, int M, int m, int f) {
-  float v = 0.0f;
+__device__ __forceinline__ float slice_sum(const float (&v)[kSlices]) {
+  float t = 0.0f;
 #pragma unroll
-  for (int s = 0; s < kSlices; ++s) v += part[((int64_t)s * M + m) * kPartStride + f];
-  return v;
+  for (int s = 0; s < kSlices; ++s) t += v[s];
+  return t;
+}
+__device__ __forceinline__ void slice_load(const float* __restrict__ part, int M, int m, int f,
+                                           float (&v)[kSlices]) {
+#pragma unroll
+  for (int s = 0; s < kSlices; ++s) v[s] = part[((int64_t)s * M + m) * kPartStride + f];
+}
+__device__ __forceinline__ float slice_sum(const float* __restrict__ part, int M, int m, int f) {
+  float v[kSlices];
+  slice_load(part, M, m, f, v);
+  return slice_sum(v);
 }
 
 hipError_t launch_fn_pack(const float* fn, int H, uint16_t* fn_packed, hipStream_t s);

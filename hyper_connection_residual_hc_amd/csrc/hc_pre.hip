@@ -53,18 +53,32 @@ hipError_t launch_sinkhorn(const float* mixes, int M, const float* scale, const 
 
 // ---- combine + RMSNorm of one row by one wavefront ------------------------------------------
 // NG = H / 512 column blocks; lane covers columns [512 g + 8 lane, +8) of each block g.
+// Up to H = 5120 the lane also holds its weight columns from the start (with the row and
+// the combine's values that still fits two waves per SIMD); wider rows load them at the end.
+template <int NG>
+constexpr bool kPreloadWeight = NG <= 10;
+
 template <int NG>
 struct RowTile {
   u32x4 r[NG][kHC];
+  u32x4 w[kPreloadWeight<NG> ? NG : 1];  // the norm weight's columns of this lane
 };
 
+// The row (streamed once, non-temporal), then the weight (shared by every row: cached). All
+// loads go out together so their latencies overlap.
 template <int NG>
-__device__ __forceinline__ void load_row(const uint16_t* __restrict__ Rr, int lane, RowTile<NG>& t) {
+__device__ __forceinline__ void load_row(const uint16_t* __restrict__ Rr,
+                                         const uint16_t* __restrict__ w, int lane,
+                                         RowTile<NG>& t) {
   constexpr int H = NG * 512;
 #pragma unroll
   for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int i = 0; i < kHC; ++i) t.r[g][i] = ld16_stream(Rr + i * H + g * 512 + lane * 8);
+  if constexpr (kPreloadWeight<NG>) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) t.w[g] = ld16(w + g * 512 + lane * 8);
+  }
 }
 
 template <int NG>
@@ -93,7 +107,10 @@ __device__ __forceinline__ void combine_norm_row(const RowTile<NG>& t, const flo
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     float wf[8], o[8];
-    unpack8(ld16(w + g * 512 + lane * 8), wf);
+    if constexpr (kPreloadWeight<NG>)
+      unpack8(t.w[g], wf);
+    else
+      unpack8(ld16(w + g * 512 + lane * 8), wf);
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (c[g][e] * rn) * wf[e];
     st16(yr + g * 512 + lane * 8, pack8(o));
@@ -112,7 +129,8 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const uint16_t* __res
   const int m = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
   if (m >= M) return;
   RowTile<NG> t;
-  load_row<NG>(R + (int64_t)m * ldR, lane, t);
+  load_row<NG>(R + (int64_t)m * ldR, w, lane, t);
+  __builtin_amdgcn_sched_barrier(0);
   float p[kHC];
 #pragma unroll
   for (int i = 0; i < kHC; ++i) p[i] = pre[(int64_t)m * ldPre + i];
@@ -131,19 +149,29 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(
   const int m = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
   if (m >= M) return;  // wave-uniform: the whole wave leaves together
   const int e = lane & 15;
-  // the row's residual loads go out first; the split + Sinkhorn below hides their latency
+  // Loads in issue order: this lane's slice partials, then the row. Vector loads complete in
+  // order, so the split + Sinkhorn waits only for the partials and runs while the row is in
+  // flight.
+  float pa[kSlices], pc[kSlices], pq[kSlices];
+  slice_load(part, M, m, e & 7, pa);
+  slice_load(part, M, m, 8 + e, pc);
+  slice_load(part, M, m, kMix, pq);
+  const float base_a = base[e & 7];
+  const float base_c = base[8 + e];
+  __builtin_amdgcn_sched_barrier(0);
   RowTile<NG> t;
-  load_row<NG>(R + (int64_t)m * ldR, lane, t);
+  load_row<NG>(R + (int64_t)m * ldR, w, lane, t);
+  __builtin_amdgcn_sched_barrier(0);
 
   // mixes for this lane's entries, reduced over the slices exactly as stats_reduce does
-  const float ss = slice_sum(part, M, m, kMix);
-  const float rs = mix_rscale(ss, kf, rms_eps);
-  const float mix_a = e < 8 ? slice_sum(part, M, m, e) * rs : 0.0f;
-  const float mix_c = slice_sum(part, M, m, 8 + e) * rs;
+  const float rs = mix_rscale(slice_sum(pq), kf, rms_eps);
+  // lanes e >= 8 carry a copy of lane e - 8's pre/post input; their pre/post value is unused
+  // (no branch here, so the loads above stay ahead of the row's)
+  const float mix_a = slice_sum(pa) * rs;
+  const float mix_c = slice_sum(pc) * rs;
   const SplitParams sp{scale[0], scale[1], scale[2], iters, pre_eps, sk_eps, post_mult};
-  const float base_a = e < 8 ? base[e] : 0.0f;
   float pp;
-  const float cv = split_sinkhorn_lane(e, mix_a, mix_c, base_a, base[8 + e], sp, &pp);
+  const float cv = split_sinkhorn_lane(e, mix_a, mix_c, base_a, base_c, sp, &pp);
   if (lane < 16) {
     comb[(int64_t)m * 16 + e] = cv;
     if (e < 4) {

@@ -52,6 +52,20 @@ def _residual(R: torch.Tensor):
     return M, H, (R.stride(0) if M else HC * H)
 
 
+def _shaped(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None:
+    """A row-strided tensor of exactly `shape` (the kernels write every element of it)."""
+    _need(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _packed(fn_packed: torch.Tensor, H: int) -> None:
+    if not isinstance(fn_packed, torch.Tensor) or fn_packed.device.type != "cuda":
+        raise ValueError("fn_packed must be a device tensor from fn_pack")
+    if not fn_packed.is_contiguous() or fn_packed.numel() * fn_packed.element_size() < fn_packed_bytes(H):
+        raise ValueError(f"fn_packed is smaller than fn_pack's output for H={H}")
+
+
 def _rows(t: torch.Tensor, width: int) -> int:
     return t.stride(0) if t.shape[0] else width
 
@@ -97,6 +111,7 @@ def pre_stats(R: torch.Tensor, fn_packed: torch.Tensor, rms_eps: float = RMS_EPS
               workspace: Optional[torch.Tensor] = None, want_sumsq: bool = True):
     """(mixes fp32 [M, 24], sumsq fp32 [M] or None)."""
     M, H, ldR = _residual(R)
+    _packed(fn_packed, H)
     if mixes is None:
         mixes = torch.empty(M, MIX, dtype=torch.float32, device=R.device)
     _contig(mixes, "mixes", torch.float32, (M, MIX))
@@ -145,7 +160,7 @@ def combine_norm(R: torch.Tensor, pre: torch.Tensor, weight: torch.Tensor,
     _contig(weight, "weight", torch.bfloat16, (H,))
     if out is None:
         out = torch.empty(M, H, dtype=torch.bfloat16, device=R.device)
-    _need(out, "out", torch.bfloat16, 2)
+    _shaped(out, "out", torch.bfloat16, (M, H))
     _lib.call("hc_combine_norm", R.data_ptr(), ldR, pre.data_ptr(), _rows(pre, HC),
               weight.data_ptr(), M, H, eps, out.data_ptr(), _rows(out, H), _stream(R))
     return out
@@ -163,6 +178,7 @@ def post(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.Tens
     _contig(comb, "comb", torch.float32, (M, HC, HC))
     if out is None:
         out = torch.empty(M, HC, H, dtype=torch.bfloat16, device=R.device)
+    _shaped(out, "out", torch.bfloat16, (M, HC, H))
     _residual(out)
     _lib.call("hc_post", x.data_ptr(), _rows(x, H), R.data_ptr(), ldR, post_.data_ptr(),
               comb.data_ptr(), M, H, out.data_ptr(), _rows(out, HC * H), _stream(R))
@@ -179,8 +195,8 @@ def mxfp8_quant_rows(y: torch.Tensor, q: Optional[torch.Tensor] = None,
         q = torch.empty(M, K, dtype=torch.uint8, device=y.device)
     if scales is None:
         scales = torch.empty(M, K // 32, dtype=torch.uint8, device=y.device)
-    _need(q, "q", torch.uint8, 2)
-    _need(scales, "scales", torch.uint8, 2)
+    _shaped(q, "q", torch.uint8, (M, K))
+    _shaped(scales, "scales", torch.uint8, (M, K // 32))
     _lib.call("mxfp8_quant_rows", y.data_ptr(), _rows(y, K), M, K, q.data_ptr(), _rows(q, K),
               scales.data_ptr(), _rows(scales, K // 32), _stream(y))
     return q, scales
@@ -208,7 +224,8 @@ def pre(R: torch.Tensor, fn_packed: torch.Tensor, scale: torch.Tensor, base: tor
                torch.empty(M, HC, HC, dtype=torch.float32, device=dev),
                torch.empty(M, HC, dtype=torch.float32, device=dev) if want_pre else None)
     y, post_, comb, pre_ = out
-    _need(y, "y", torch.bfloat16, 2)
+    _packed(fn_packed, H)
+    _shaped(y, "y", torch.bfloat16, (M, H))
     _contig(post_, "post", torch.float32, (M, HC))
     _contig(comb, "comb", torch.float32, (M, HC, HC))
     if pre_ is not None:
@@ -251,8 +268,10 @@ def post_pre(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.
                torch.empty(M, HC, HC, dtype=torch.float32, device=dev),
                torch.empty(M, HC, dtype=torch.float32, device=dev) if want_pre else None)
     Rn, y, post_o, comb_o, pre_o = out
+    _packed(fn_packed, H)
+    _shaped(Rn, "R_out", torch.bfloat16, (M, HC, H))
     _, _, ldOut = _residual(Rn)
-    _need(y, "y", torch.bfloat16, 2)
+    _shaped(y, "y", torch.bfloat16, (M, H))
     _contig(post_o, "post_out", torch.float32, (M, HC))
     _contig(comb_o, "comb_out", torch.float32, (M, HC, HC))
     if pre_o is not None:
@@ -265,3 +284,58 @@ def post_pre(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.
               post_o.data_ptr(), comb_o.data_ptr(), ws.data_ptr(),
               ws.numel() * ws.element_size(), _stream(R))
     return Rn, y, post_o, comb_o, pre_o
+
+
+# ---- the two halves of the fused post -> pre ----------------------------------------------------
+def post_stats(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.Tensor,
+               fn_packed: torch.Tensor, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None):
+    """First half of post_pre: (R' [M, 4, H], workspace holding R''s mix-stat partials under
+    the next site's fn_packed). Pass both to pre_finish."""
+    M, H, ldR = _residual(R)
+    _need(x, "x", torch.bfloat16, 2)
+    if tuple(x.shape) != (M, H):
+        raise ValueError(f"x must be [{M}, {H}]")
+    _contig(post_, "post", torch.float32, (M, HC))
+    _contig(comb, "comb", torch.float32, (M, HC, HC))
+    _packed(fn_packed, H)
+    if out is None:
+        out = torch.empty(M, HC, H, dtype=torch.bfloat16, device=R.device)
+    _shaped(out, "out", torch.bfloat16, (M, HC, H))
+    _, _, ldOut = _residual(out)
+    ws = _workspace(post_pre_workspace_bytes(M, H), R.device, workspace)
+    _lib.call("hc_post_stats", x.data_ptr(), _rows(x, H), R.data_ptr(), ldR, post_.data_ptr(),
+              comb.data_ptr(), fn_packed.data_ptr(), M, H, out.data_ptr(), ldOut, ws.data_ptr(),
+              ws.numel() * ws.element_size(), _stream(R))
+    return out, ws
+
+
+def pre_finish(R: torch.Tensor, workspace: torch.Tensor, scale: torch.Tensor,
+               base: torch.Tensor, weight: torch.Tensor, rms_eps: float = RMS_EPS,
+               pre_eps: float = HC_EPS, sinkhorn_eps: float = HC_EPS, iters: int = ITERS,
+               post_mult: float = POST_MULT, norm_eps: float = RMS_EPS, want_pre: bool = False,
+               out=None):
+    """Second half of post_pre, on post_stats's (R', workspace):
+    (y bf16 [M, H], post [M, 4], comb [M, 4, 4], pre [M, 4] or None)."""
+    M, H, ldR = _residual(R)
+    _contig(scale, "scale", torch.float32, (3,))
+    _contig(base, "base", torch.float32, (MIX,))
+    _contig(weight, "weight", torch.bfloat16, (H,))
+    dev = R.device
+    if out is None:
+        out = (torch.empty(M, H, dtype=torch.bfloat16, device=dev),
+               torch.empty(M, HC, dtype=torch.float32, device=dev),
+               torch.empty(M, HC, HC, dtype=torch.float32, device=dev),
+               torch.empty(M, HC, dtype=torch.float32, device=dev) if want_pre else None)
+    y, post_o, comb_o, pre_o = out
+    _shaped(y, "y", torch.bfloat16, (M, H))
+    _contig(post_o, "post", torch.float32, (M, HC))
+    _contig(comb_o, "comb", torch.float32, (M, HC, HC))
+    if pre_o is not None:
+        _contig(pre_o, "pre", torch.float32, (M, HC))
+    _lib.call("hc_pre_finish", R.data_ptr(), ldR, scale.data_ptr(), base.data_ptr(),
+              weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult,
+              norm_eps, y.data_ptr(), _rows(y, H), _ptr(pre_o), post_o.data_ptr(),
+              comb_o.data_ptr(), workspace.data_ptr(),
+              workspace.numel() * workspace.element_size(), _stream(R))
+    return y, post_o, comb_o, pre_o

@@ -193,6 +193,32 @@ HC_API int hc_post_pre(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_
                        float* post_out, float* comb_out, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * hc_post_pre in two calls, for callers that place other work between the halves or time
+ * them apart. hc_post_stats followed by hc_pre_finish on the same stream, with the same
+ * workspace, M and H and with hc_pre_finish's R = hc_post_stats's Rout (same pointer and
+ * stride), gives exactly the bits of hc_post_pre.
+ *
+ * hc_post_stats: Rout = hc_post(x, R, post, comb) (bit-identical to hc_post), and in
+ *   `workspace` a record of Rout's mix-stat partial sums under the next site's fn_packed.
+ *   Arguments as hc_post_pre. H: as hc_pre.
+ * hc_pre_finish: reads that record and Rout; writes y, pre (or NULL), post, comb as hc_pre on
+ *   Rout would. The record is opaque; a workspace that no hc_post_stats call with this M and
+ *   H filled gives unspecified values (never an out-of-bounds access).
+ * workspace: >= hc_post_pre_workspace_bytes(M, H), 256-byte aligned, written by the first
+ *   call and read by the second.
+ * ------------------------------------------------------------------------------------- */
+HC_API int hc_post_stats(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                         const float* post, const float* comb, const uint16_t* fn_packed,
+                         int64_t M, int32_t H, uint16_t* Rout, int64_t ldOut, void* workspace,
+                         size_t workspace_bytes, void* stream);
+HC_API int hc_pre_finish(const uint16_t* R, int64_t ldR, const float* scale, const float* base,
+                         const uint16_t* weight, int64_t M, int32_t H, float rms_eps,
+                         float pre_eps, float sinkhorn_eps, int32_t iters, float post_mult,
+                         float norm_eps, uint16_t* y, int64_t ldY, float* pre, float* post,
+                         float* comb, const void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -79,3 +79,30 @@ def test_validation_codes(L):
     # workspace too small
     assert L.hc_pre_stats(fake, 4 * H, fake, 5, H, 1e-6, ctypes.c_void_p(0x800000), None,
                           ctypes.c_void_p(0x700000), 16, None) == 5
+
+
+def test_validation_codes_of_the_post_pre_halves(L):
+    H = 5120
+    fake = ctypes.c_void_p(0x10000)
+    a, b, c, d = (ctypes.c_void_p(v) for v in (0x1000000, 0x2000000, 0x3000000, 0x4000000))
+    ws = ctypes.c_void_p(0x5000000)
+    need = L.hc_post_pre_workspace_bytes(7, H)
+    assert need == 8 * 7 * 32 * 4
+    # M = 0 no-ops
+    assert L.hc_post_stats(None, 0, None, 0, None, None, None, 0, H, None, 0, None, 0, None) == 0
+    assert L.hc_pre_finish(None, 0, None, None, None, 0, H, 1e-6, 1e-6, 1e-6, 20, 2.0, 1e-6,
+                           None, 0, None, None, None, None, 0, None) == 0
+    # NULL, shape, workspace, alias
+    assert L.hc_post_stats(None, H, fake, 4 * H, fake, fake, fake, 7, H, fake, 4 * H, ws, need,
+                           None) == 1
+    assert L.hc_post_stats(a, H, b, 4 * H, c, c, d, 7, 512 * 3, fake, 4 * H, ws, need, None) == 2
+    assert L.hc_post_stats(a, H, b, 4 * H, c, c, d, 7, H, fake, 4 * H, ws, need - 4, None) == 5
+    assert L.hc_post_stats(a, H, b, 4 * H, c, ctypes.c_void_p(0x3000040), d, 7, H, b, 4 * H, ws,
+                           need, None) == 4
+    assert L.hc_pre_finish(a, 4 * H, b, c, d, 7, H, 1e-6, 1e-6, 1e-6, 0, 2.0, 1e-6, fake, H,
+                           None, fake, fake, ws, need, None) == 2
+    assert L.hc_pre_finish(a, 4 * H, b, c, d, 7, H, 1e-6, 1e-6, 1e-6, 20, 2.0, 1e-6, fake, H,
+                           None, fake, fake, None, need, None) == 5
+    # the workspace is an input of the second half: y over it is an alias
+    assert L.hc_pre_finish(a, 4 * H, b, c, d, 7, H, 1e-6, 1e-6, 1e-6, 20, 2.0, 1e-6, ws, H,
+                           None, fake, ctypes.c_void_p(0x6000000), ws, need, None) == 4

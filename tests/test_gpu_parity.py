@@ -291,3 +291,45 @@ def test_fused_post_pre_matches_oracle(attn, ffn):
     for name, g in (("pre", pre2), ("post", post2), ("comb", comb2)):
         err = np.abs(gu.f32_np(g) - ref2[name]).max()
         assert err <= 2e-3, f"{name} ffn (chain): {err}"
+
+
+@pytest.mark.parametrize("M", [65, 4096])
+def test_post_stats_then_pre_finish_equals_post_pre(attn, ffn, M):
+    """The two-call form gives the bits of hc_post_pre, also with unrelated work on the stream
+    between the halves (here: an hc_post of other rows into another buffer)."""
+    gu.say(f"hc_post_stats + hc_pre_finish M={M}")
+    R = gu.dev(inputs.residual(M, M + 7))
+    x = gu.dev(inputs.sublayer_out(M, M + 8))
+    _, post, comb, _ = ops.pre(R, attn.fnp, attn.scale_d, attn.base_d, attn.w_d)
+    full = ops.post_pre(x, R, post, comb, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d,
+                        want_pre=True)
+    Rn, ws = ops.post_stats(x, R, post, comb, ffn.fnp, out=_poison_bf16(M, 4, gu.H))
+    other = ops.post(x, R, post, comb)
+    y, post2, comb2, pre2 = ops.pre_finish(Rn, ws, ffn.scale_d, ffn.base_d, ffn.w_d,
+                                           want_pre=True,
+                                           out=(_poison_bf16(M, gu.H), _poison_f32(M, 4),
+                                                _poison_f32(M, 4, 4), _poison_f32(M, 4)))
+    assert torch.equal(Rn.view(torch.int16), full[0].view(torch.int16))
+    assert torch.equal(other.view(torch.int16), full[0].view(torch.int16))
+    assert torch.equal(y.view(torch.int16), full[1].view(torch.int16))
+    assert torch.equal(post2, full[2]) and torch.equal(comb2, full[3]) and torch.equal(pre2, full[4])
+
+
+def test_binding_rejects_short_outputs(attn, ffn):
+    """The binding checks every output's shape against the inputs before the call (the C ABI
+    receives bare pointers and cannot)."""
+    M = 64
+    R = gu.dev(inputs.residual(M, 3))
+    x = gu.dev(inputs.sublayer_out(M, 4))
+    _, post, comb, _ = ops.pre(R, attn.fnp, attn.scale_d, attn.base_d, attn.w_d)
+    short_y = torch.empty(M - 1, gu.H, dtype=torch.bfloat16, device=R.device)
+    with pytest.raises(ValueError):
+        ops.pre(R, attn.fnp, attn.scale_d, attn.base_d, attn.w_d,
+                out=(short_y, post.clone(), comb.clone(), None))
+    with pytest.raises(ValueError):
+        ops.post(x, R, post, comb, out=torch.empty(M - 1, 4, gu.H, dtype=torch.bfloat16,
+                                                   device=R.device))
+    with pytest.raises(ValueError):
+        ops.combine_norm(R, post, attn.w_d, out=short_y)
+    with pytest.raises(ValueError):
+        ops.pre_stats(R, attn.fnp[:-8])
