@@ -41,7 +41,7 @@ PEAK_HBM_GBS = 8000.0
 # algorithmic bytes per row (what the method must move at least once)
 POST_BYTES_ROW = 2 * (HC * H + H + HC * H) + 4 * (HC + HC * HC)  # R + x in, R' out, post + comb
 PRE_BYTES_ROW = 2 * (HC * H + H) + 4 * (HC + HC + HC * HC)  # R in, y out, pre/post/comb out
-FN_BYTES = 24 * 4 * H * 4  # fn once per call (fp32 layout; the packed bf16 parts cost 1.25x)
+FN_BYTES = 24 * 4 * H * 4  # fn once per call (fp32 layout; the packed bf16 parts are 1.67x)
 PRE_BYTES_CALL = FN_BYTES + 2 * H  # fn and the norm weight, once per call
 STEP_BYTES = M_BENCH * (POST_BYTES_ROW + PRE_BYTES_ROW) + PRE_BYTES_CALL
 # the dominant kernel of each path and the algorithmic bytes one launch moves

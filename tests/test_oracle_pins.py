@@ -418,3 +418,40 @@ def test_hc_head_zero_scale_closed_form():
     xv = o.bf16_to_f64(inputs.bits(R))
     want = sum(pre[i] * xv[:, i, :] for i in range(4))
     np.testing.assert_allclose(y, want, rtol=1e-14)
+
+
+# ------------------------------------------------------------------------------------------
+# 128x4 scale swizzle (prefill_sp.py, swizzle_128x4 docstring: tile (m // 128, g // 4) in
+# row-tile-major order, inside a tile [m % 32][(m % 128) // 32][g % 4], rows zero-padded)
+# ------------------------------------------------------------------------------------------
+def _swizzle_position(m, g, G):
+    tile = (m // 128) * (G // 4) + g // 4
+    return tile * 512 + (m % 32) * 16 + ((m % 128) // 32) * 4 + g % 4
+
+
+@pytest.mark.parametrize("M,G", [(1, 4), (130, 8), (256, 12)])
+def test_swizzle_128x4_places_every_byte_by_the_stated_layout(M, G):
+    rng = np.random.default_rng(M * 100 + G)
+    sf = rng.integers(1, 256, size=(M, G), dtype=np.uint8)  # no zero: padding is told apart
+    out = o.swizzle_128x4(sf)
+    mt = (M + 127) // 128
+    assert out.shape == (mt * 128 * G,)
+    seen = np.zeros(out.shape, dtype=bool)
+    for m in range(M):
+        for g in range(G):
+            p = _swizzle_position(m, g, G)
+            assert out[p] == sf[m, g], (m, g, p)
+            seen[p] = True
+    assert np.all(out[~seen] == 0)  # the padded rows are zero and nothing else is left
+
+
+def test_swizzle_128x4_hand_positions():
+    """Positions worked out by hand from the stated layout, M = 130, G = 8 (two row tiles,
+    two column tiles): (m, g) = (33, 5) -> tile 1, row-in-32 1, quarter 1, col 1 -> 533;
+    (129, 2) -> tile 2, row-in-32 1, quarter 0, col 2 -> 1042; (0, 0) -> 0; (127, 7) ->
+    tile 1, 31 * 16 + 3 * 4 + 3 = 511 -> 1023."""
+    sf = np.zeros((130, 8), dtype=np.uint8)
+    sf[33, 5], sf[129, 2], sf[0, 0], sf[127, 7] = 7, 9, 11, 13
+    out = o.swizzle_128x4(sf)
+    assert out[533] == 7 and out[1042] == 9 and out[0] == 11 and out[1023] == 13
+    assert np.count_nonzero(out) == 4
