@@ -164,17 +164,23 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
     const int hg = lane & 7;
     u32x4 ld0[kItemsPerLane][kHC + 1], ld1[kItemsPerLane][kHC + 1];
     u32x4 ld2[kItemsPerLane][kHC + 1], ld3[kItemsPerLane][kHC + 1];
+    // The loop issues loads four stages ahead, also past the last stage, so that it has no
+    // branch around them (the in-order load counters then stay exact). Those unused loads read
+    // this block's packed fn slice, which the consumers keep in the L2, not HBM. (A slice
+    // holds 40H elements; the loads span 3H + 512.)
+    const uint16_t* dead = a.fnp + (int64_t)s * chunks_per_slice(H) * kPackTiles * 64 * 8 + lane * 8;
     auto issue = [&](int sigma, u32x4 (&d)[kItemsPerLane][kHC + 1]) {
-      const int sg = min(sigma, total - 1);  // past the end: reload the last stage (unused)
+      const bool live = sigma < total;  // block-uniform
+      const int sg = min(sigma, total - 1);
       const int T = tile_of(sg), p = sg - (sg / nstage) * nstage;
       const int h = hs + 64 * p + 8 * hg;
 #pragma unroll
       for (int it = 0; it < kItemsPerLane; ++it) {
         const int row = min(T * kStatsRows + 16 * wave + 8 * it + (lane >> 3), M - 1);
-        const uint16_t* rr = a.R + (int64_t)row * a.ldR + h;
+        const uint16_t* rr = live ? a.R + (int64_t)row * a.ldR + h : dead;
 #pragma unroll
         for (int i = 0; i < kHC; ++i) d[it][i] = ld16_stream(rr + (int64_t)i * H);
-        if (kPost) d[it][kHC] = ld16_stream(a.x + (int64_t)row * a.ldX + h);
+        if (kPost) d[it][kHC] = ld16_stream(live ? a.x + (int64_t)row * a.ldX + h : dead);
       }
     };
     auto produce = [&](int sigma, u32x4 (&d)[kItemsPerLane][kHC + 1]) {
@@ -230,33 +236,41 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
     issue(2, ld2);
     issue(3, ld3);
     __syncthreads();  // the consumers' first coefficient tile is in LDS
-    // four iterations per trip so the four load buffers keep fixed registers; stage sigma's
-    // loads were issued four iterations earlier
-    for (int sigma = 0; sigma <= total; sigma += 4) {
-      if (sigma < total) {
-        produce(sigma, ld0);
-        issue(sigma + 4, ld0);
-      }
+    // Full trips of four stages (four load buffers in fixed registers); stage sigma's loads
+    // were issued four stages earlier. The trip has no branch: every path from one stage to
+    // the next issues the same memory operations, so the compiler's in-order wait counts stay
+    // exact and each stage waits only for its own loads, not for the three stages behind it.
+    int sigma = 0;
+    for (; sigma + 4 <= total; sigma += 4) {
+      produce(sigma, ld0);
+      issue(sigma + 4, ld0);
       __syncthreads();
-      if (sigma + 1 > total) break;
-      if (sigma + 1 < total) {
-        produce(sigma + 1, ld1);
-        issue(sigma + 5, ld1);
-      }
+      produce(sigma + 1, ld1);
+      issue(sigma + 5, ld1);
       __syncthreads();
-      if (sigma + 2 > total) break;
-      if (sigma + 2 < total) {
-        produce(sigma + 2, ld2);
-        issue(sigma + 6, ld2);
-      }
+      produce(sigma + 2, ld2);
+      issue(sigma + 6, ld2);
       __syncthreads();
-      if (sigma + 3 > total) break;
-      if (sigma + 3 < total) {
-        produce(sigma + 3, ld3);
-        issue(sigma + 7, ld3);
-      }
+      produce(sigma + 3, ld3);
+      issue(sigma + 7, ld3);
       __syncthreads();
     }
+    // the last total % 4 stages (already loaded), then the barrier that closes the consumers'
+    // last stage: total + 2 barriers in all, as the consumers
+    const int rest = total - sigma;
+    if (rest > 0) {
+      produce(sigma, ld0);
+      __syncthreads();
+    }
+    if (rest > 1) {
+      produce(sigma + 1, ld1);
+      __syncthreads();
+    }
+    if (rest > 2) {
+      produce(sigma + 2, ld2);
+      __syncthreads();
+    }
+    __syncthreads();
   } else {
     // ===================================== consumers ======================================
     const int q = wave - 4;  // stream
