@@ -240,20 +240,26 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
     // were issued four stages earlier. The trip has no branch: every path from one stage to
     // the next issues the same memory operations, so the compiler's in-order wait counts stay
     // exact and each stage waits only for its own loads, not for the three stages behind it.
+    auto trip = [&](int sg) {
+      produce(sg, ld0);
+      issue(sg + 4, ld0);
+      __syncthreads();
+      produce(sg + 1, ld1);
+      issue(sg + 5, ld1);
+      __syncthreads();
+      produce(sg + 2, ld2);
+      issue(sg + 6, ld2);
+      __syncthreads();
+      produce(sg + 3, ld3);
+      issue(sg + 7, ld3);
+      __syncthreads();
+    };
+    // The first trip is peeled: the loop is then entered in the same state it loops back in,
+    // so the compiler's wait counts are those of the steady state.
     int sigma = 0;
-    for (; sigma + 4 <= total; sigma += 4) {
-      produce(sigma, ld0);
-      issue(sigma + 4, ld0);
-      __syncthreads();
-      produce(sigma + 1, ld1);
-      issue(sigma + 5, ld1);
-      __syncthreads();
-      produce(sigma + 2, ld2);
-      issue(sigma + 6, ld2);
-      __syncthreads();
-      produce(sigma + 3, ld3);
-      issue(sigma + 7, ld3);
-      __syncthreads();
+    if (total >= 4) {
+      trip(0);
+      for (sigma = 4; sigma + 4 <= total; sigma += 4) trip(sigma);
     }
     // the last total % 4 stages (already loaded), then the barrier that closes the consumers'
     // last stage: total + 2 barriers in all, as the consumers
