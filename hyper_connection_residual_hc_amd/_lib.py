@@ -43,6 +43,16 @@ SIGNATURES = {
     "hc_post_stats": (_int, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _i32, _p, _i64, _p, _sz, _p]),
     "hc_pre_finish": (_int, [_p, _i64, _p, _p, _p, _i64, _i32, _f32, _f32, _f32, _i32, _f32, _f32,
                              _p, _i64, _p, _p, _p, _p, _sz, _p]),
+    "hc_pre_mxfp8": (_int, [_p, _i64, _p, _p, _p, _p, _i64, _i32, _f32, _f32, _f32, _i32, _f32,
+                            _f32, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _p, _sz, _p]),
+    "hc_post_pre_mxfp8": (_int, [_p, _i64, _p, _i64, _p, _p, _p, _p, _p, _p, _i64, _i32, _f32,
+                                 _f32, _f32, _i32, _f32, _f32, _p, _i64, _p, _i64, _p, _i64, _p,
+                                 _i64, _p, _p, _p, _p, _sz, _p]),
+    "hc_pre_finish_mxfp8": (_int, [_p, _i64, _p, _p, _p, _i64, _i32, _f32, _f32, _f32, _i32,
+                                   _f32, _f32, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _p, _sz,
+                                   _p]),
+    "mxfp8_swizzled_bytes": (_sz, [_i64, _i32]),
+    "mxfp8_swizzle_128x4": (_int, [_p, _i64, _i64, _i32, _p, _p]),
 }
 
 _LIB = None

@@ -47,6 +47,178 @@ int check_residual(const uint16_t* R, int64_t ldR, int32_t H) {
   return HC_OK;
 }
 
+
+// Disjointness of outputs from inputs and from each other (empty spans are skipped).
+int no_alias(const Span* ins, int nin, const Span* outs, int nout) {
+  for (int i = 0; i < nout; ++i) {
+    if (outs[i].b == outs[i].e) continue;
+    for (int j = 0; j < nin; ++j)
+      if (ins[j].b != ins[j].e && overlaps(outs[i], ins[j])) return HC_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (outs[j].b != outs[j].e && overlaps(outs[i], outs[j])) return HC_ERR_ALIAS;
+  }
+  return HC_OK;
+}
+
+// What the finish (split + Sinkhorn + combine + RMSNorm) takes and writes. y is bf16 [M, H];
+// with mx, q / sc are y's MXFP8 codes [M, H] and scales [M, H/32] and y may be NULL.
+struct Finish {
+  const float* scale;
+  const float* base;
+  const uint16_t* weight;
+  float rms_eps, pre_eps, sk_eps;
+  int32_t iters;
+  float post_mult, norm_eps;
+  uint16_t* y;
+  int64_t ldY;
+  uint8_t* q;
+  int64_t ldQ;
+  uint8_t* sc;
+  int64_t ldS;
+  float* pre;
+  float* post;
+  float* comb;
+};
+
+// Scalar checks (before the M == 0 no-op).
+int finish_scalars(const Finish& f, int32_t H) {
+  if (!stats_h_ok(H) || !hc::combine_h_supported(H)) return HC_ERR_SHAPE;
+  if (f.iters < 1 || f.iters > 100000) return HC_ERR_SHAPE;
+  if (!finite_nonneg(f.rms_eps) || !finite_nonneg(f.pre_eps) || !finite_nonneg(f.sk_eps) ||
+      !finite_nonneg(f.norm_eps) || !isfinite(f.post_mult))
+    return HC_ERR_ARG;
+  return HC_OK;
+}
+
+// Pointer, stride and alignment checks; fills the finish's 3 input and 6 output spans.
+int finish_pointers(const Finish& f, int64_t M, int32_t H, bool mx, Span* ins, Span* outs) {
+  if (!f.scale || !f.base || !f.weight || !f.post || !f.comb) return HC_ERR_NULL;
+  if (!mx && !f.y) return HC_ERR_NULL;
+  if (mx && (!f.q || !f.sc)) return HC_ERR_NULL;
+  if (f.y && f.ldY < H) return HC_ERR_SHAPE;
+  if (mx && (f.ldQ < H || f.ldS < H / 32)) return HC_ERR_SHAPE;
+  if (!al16(f.weight)) return HC_ERR_ALIGN;
+  if (f.y && (!al16(f.y) || (f.ldY * 2) % 16)) return HC_ERR_ALIGN;
+  if (mx && (!al16(f.q) || f.ldQ % 16)) return HC_ERR_ALIGN;
+  ins[0] = Span{(uintptr_t)f.scale, (uintptr_t)f.scale + 12};
+  ins[1] = Span{(uintptr_t)f.base, (uintptr_t)f.base + kMix * 4};
+  ins[2] = Span{(uintptr_t)f.weight, (uintptr_t)f.weight + (uintptr_t)H * 2};
+  outs[0] = f.y ? rows_span(f.y, M, f.ldY, H, 2) : Span{0, 0};
+  outs[1] = rows_span(f.post, M, kHC, kHC, 4);
+  outs[2] = rows_span(f.comb, M, kHC * kHC, kHC * kHC, 4);
+  outs[3] = f.pre ? rows_span(f.pre, M, kHC, kHC, 4) : Span{0, 0};
+  outs[4] = mx ? rows_span(f.q, M, f.ldQ, H, 1) : Span{0, 0};
+  outs[5] = mx ? rows_span(f.sc, M, f.ldS, H / 32, 1) : Span{0, 0};
+  return HC_OK;
+}
+
+int workspace_ok(const void* ws, size_t bytes, int64_t M) {
+  if (!ws || bytes < hc::stats_workspace_bytes(M)) return HC_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return HC_ERR_ALIGN;
+  return HC_OK;
+}
+
+Span workspace_span(const void* ws, int64_t M) {
+  return Span{(uintptr_t)ws, (uintptr_t)ws + hc::stats_workspace_bytes(M)};
+}
+
+hipError_t launch_finish(const float* part, const uint16_t* R, int64_t ldR, const Finish& f,
+                         int64_t M, int32_t H, bool mx, hipStream_t s) {
+  return hc::launch_pre_finish(part, R, ldR, f.scale, f.base, f.weight, (int)M, H, f.rms_eps,
+                               f.pre_eps, f.sk_eps, f.iters, f.post_mult, f.norm_eps, f.y, f.ldY,
+                               mx ? f.q : nullptr, f.ldQ, mx ? f.sc : nullptr, f.ldS, f.pre,
+                               f.post, f.comb, s);
+}
+
+// hc_pre: stats of R into the workspace, then the finish.
+int pre_impl(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, int64_t M, int32_t H,
+             const Finish& f, bool mx, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if ((st = finish_scalars(f, H))) return st;
+  if (M == 0) return HC_OK;
+  if (!R || !fn_packed) return HC_ERR_NULL;
+  Span ins[5], outs[7];
+  if ((st = finish_pointers(f, M, H, mx, ins, outs))) return st;
+  if ((st = check_residual(R, ldR, H))) return st;
+  if (!al16(fn_packed)) return HC_ERR_ALIGN;
+  if ((st = workspace_ok(workspace, workspace_bytes, M))) return st;
+  ins[3] = rows_span(R, M, ldR, (int64_t)kHC * H, 2);
+  ins[4] = Span{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)};
+  outs[6] = workspace_span(workspace, M);
+  if ((st = no_alias(ins, 5, outs, 7))) return st;
+  float* part = static_cast<float*>(workspace);
+  hipStream_t s = as_stream(stream);
+  if ((st = launched(hc::launch_stats(R, ldR, fn_packed, (int)M, H, part, s)))) return st;
+  return launched(launch_finish(part, R, ldR, f, M, H, mx, s));
+}
+
+// hc_pre_finish: the finish from a workspace filled by hc_post_stats.
+int finish_impl(const uint16_t* R, int64_t ldR, int64_t M, int32_t H, const Finish& f, bool mx,
+                const void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if ((st = finish_scalars(f, H))) return st;
+  if (M == 0) return HC_OK;
+  if (!R) return HC_ERR_NULL;
+  Span ins[5], outs[6];
+  if ((st = finish_pointers(f, M, H, mx, ins, outs))) return st;
+  if ((st = check_residual(R, ldR, H))) return st;
+  if ((st = workspace_ok(workspace, workspace_bytes, M))) return st;
+  ins[3] = rows_span(R, M, ldR, (int64_t)kHC * H, 2);
+  ins[4] = workspace_span(workspace, M);
+  if ((st = no_alias(ins, 5, outs, 6))) return st;
+  return launched(launch_finish(static_cast<const float*>(workspace), R, ldR, f, M, H, mx,
+                                as_stream(stream)));
+}
+
+// hc_post_stats's checks; fills its 5 input and 2 output spans.
+int post_stats_check(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                     const float* post, const float* comb, const uint16_t* fn_packed, int64_t M,
+                     int32_t H, uint16_t* Rout, int64_t ldOut, const void* workspace,
+                     size_t workspace_bytes, Span* ins, Span* outs) {
+  int st;
+  if (!x || !R || !post || !comb || !fn_packed || !Rout) return HC_ERR_NULL;
+  if ((st = check_residual(R, ldR, H))) return st;
+  if (ldX < H || ldOut < (int64_t)kHC * H) return HC_ERR_SHAPE;
+  if (!al16(x) || !al16(Rout) || !al16(post) || !al16(comb) || !al16(fn_packed) ||
+      (ldX * 2) % 16 || (ldOut * 2) % 16)
+    return HC_ERR_ALIGN;
+  if ((st = workspace_ok(workspace, workspace_bytes, M))) return st;
+  ins[0] = rows_span(x, M, ldX, H, 2);
+  ins[1] = rows_span(R, M, ldR, (int64_t)kHC * H, 2);
+  ins[2] = rows_span(post, M, kHC, kHC, 4);
+  ins[3] = rows_span(comb, M, kHC * kHC, kHC * kHC, 4);
+  ins[4] = Span{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)};
+  outs[0] = rows_span(Rout, M, ldOut, (int64_t)kHC * H, 2);
+  outs[1] = workspace_span(workspace, M);
+  return HC_OK;
+}
+
+// hc_post_pre: hc_post_stats then the finish on Rout.
+int post_pre_impl(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                  const float* post, const float* comb, const uint16_t* fn_packed, int64_t M,
+                  int32_t H, uint16_t* Rout, int64_t ldOut, const Finish& f, bool mx,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if (!post_h_ok(H)) return HC_ERR_SHAPE;
+  if ((st = finish_scalars(f, H))) return st;
+  if (M == 0) return HC_OK;
+  Span ins[8], outs[8];
+  if ((st = post_stats_check(x, ldX, R, ldR, post, comb, fn_packed, M, H, Rout, ldOut, workspace,
+                             workspace_bytes, ins, outs)))
+    return st;
+  if ((st = finish_pointers(f, M, H, mx, ins + 5, outs + 2))) return st;
+  if ((st = no_alias(ins, 8, outs, 8))) return st;
+  float* part = static_cast<float*>(workspace);
+  hipStream_t s = as_stream(stream);
+  if ((st = launched(hc::launch_post_stats(x, ldX, R, ldR, post, comb, fn_packed, (int)M, H, Rout,
+                                           ldOut, part, s))))
+    return st;
+  return launched(launch_finish(part, Rout, ldOut, f, M, H, mx, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -219,42 +391,21 @@ HC_API int hc_pre(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, con
                   float post_mult, float norm_eps, uint16_t* y, int64_t ldY, float* pre,
                   float* post, float* comb, void* workspace, size_t workspace_bytes,
                   void* stream) {
-  int st = check_m(M);
-  if (st) return st;
-  if (!stats_h_ok(H) || !hc::combine_h_supported(H)) return HC_ERR_SHAPE;
-  if (iters < 1 || iters > 100000) return HC_ERR_SHAPE;
-  if (!finite_nonneg(rms_eps) || !finite_nonneg(pre_eps) || !finite_nonneg(sinkhorn_eps) ||
-      !finite_nonneg(norm_eps) || !isfinite(post_mult))
-    return HC_ERR_ARG;
-  if (M == 0) return HC_OK;
-  if (!R || !fn_packed || !scale || !base || !weight || !y || !post || !comb) return HC_ERR_NULL;
-  if ((st = check_residual(R, ldR, H))) return st;
-  if (ldY < H) return HC_ERR_SHAPE;
-  if (!al16(fn_packed) || !al16(weight) || !al16(y) || (ldY * 2) % 16) return HC_ERR_ALIGN;
-  if (!workspace || workspace_bytes < hc::stats_workspace_bytes(M)) return HC_ERR_WORKSPACE;
-  if (((uintptr_t)workspace & 255u) != 0) return HC_ERR_ALIGN;
-  const Span ins[5] = {rows_span(R, M, ldR, (int64_t)kHC * H, 2),
-                       Span{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)},
-                       Span{(uintptr_t)scale, (uintptr_t)scale + 12},
-                       Span{(uintptr_t)base, (uintptr_t)base + kMix * 4},
-                       Span{(uintptr_t)weight, (uintptr_t)weight + (uintptr_t)H * 2}};
-  Span outs[5] = {rows_span(y, M, ldY, H, 2), rows_span(post, M, kHC, kHC, 4),
-                  rows_span(comb, M, kHC * kHC, kHC * kHC, 4),
-                  Span{(uintptr_t)workspace, (uintptr_t)workspace + hc::stats_workspace_bytes(M)},
-                  pre ? rows_span(pre, M, kHC, kHC, 4) : Span{0, 0}};
-  for (int i = 0; i < 5; ++i) {
-    if (outs[i].b == outs[i].e) continue;
-    for (int j = 0; j < 5; ++j)
-      if (overlaps(outs[i], ins[j])) return HC_ERR_ALIAS;
-    for (int j = i + 1; j < 5; ++j)
-      if (outs[j].b != outs[j].e && overlaps(outs[i], outs[j])) return HC_ERR_ALIAS;
-  }
-  float* part = static_cast<float*>(workspace);
-  hipStream_t s = as_stream(stream);
-  if ((st = launched(hc::launch_stats(R, ldR, fn_packed, (int)M, H, part, s)))) return st;
-  return launched(hc::launch_pre_finish(part, R, ldR, scale, base, weight, (int)M, H, rms_eps,
-                                        pre_eps, sinkhorn_eps, iters, post_mult, norm_eps, y, ldY,
-                                        pre, post, comb, s));
+  const Finish f{scale, base, weight, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult, norm_eps,
+                 y, ldY, nullptr, 0, nullptr, 0, pre, post, comb};
+  return pre_impl(R, ldR, fn_packed, M, H, f, false, workspace, workspace_bytes, stream);
+}
+
+HC_API int hc_pre_mxfp8(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed,
+                        const float* scale, const float* base, const uint16_t* weight, int64_t M,
+                        int32_t H, float rms_eps, float pre_eps, float sinkhorn_eps,
+                        int32_t iters, float post_mult, float norm_eps, uint16_t* y, int64_t ldY,
+                        uint8_t* q, int64_t ldQ, uint8_t* scales, int64_t ldS, float* pre,
+                        float* post, float* comb, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const Finish f{scale, base, weight, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult, norm_eps,
+                 y, ldY, q, ldQ, scales, ldS, pre, post, comb};
+  return pre_impl(R, ldR, fn_packed, M, H, f, true, workspace, workspace_bytes, stream);
 }
 
 // ---- fused post -> pre -----------------------------------------------------------------------
@@ -270,54 +421,26 @@ HC_API int hc_post_pre(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_
                        int64_t ldOut, uint16_t* y, int64_t ldY, float* pre_out,
                        float* post_out, float* comb_out, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  int st = check_m(M);
-  if (st) return st;
-  if (!stats_h_ok(H) || !hc::combine_h_supported(H) || !post_h_ok(H)) return HC_ERR_SHAPE;
-  if (iters < 1 || iters > 100000) return HC_ERR_SHAPE;
-  if (!finite_nonneg(rms_eps) || !finite_nonneg(pre_eps) || !finite_nonneg(sinkhorn_eps) ||
-      !finite_nonneg(norm_eps) || !isfinite(post_mult))
-    return HC_ERR_ARG;
-  if (M == 0) return HC_OK;
-  if (!x || !R || !post || !comb || !fn_packed || !scale || !base || !weight || !Rout || !y ||
-      !post_out || !comb_out)
-    return HC_ERR_NULL;
-  if ((st = check_residual(R, ldR, H))) return st;
-  if (ldX < H || ldOut < (int64_t)kHC * H || ldY < H) return HC_ERR_SHAPE;
-  if (!al16(x) || !al16(Rout) || !al16(y) || !al16(post) || !al16(comb) || !al16(fn_packed) ||
-      !al16(weight) || (ldX * 2) % 16 || (ldOut * 2) % 16 || (ldY * 2) % 16)
-    return HC_ERR_ALIGN;
-  if (!workspace || workspace_bytes < hc::stats_workspace_bytes(M)) return HC_ERR_WORKSPACE;
-  if (((uintptr_t)workspace & 255u) != 0) return HC_ERR_ALIGN;
-  const Span ins[8] = {rows_span(x, M, ldX, H, 2),
-                       rows_span(R, M, ldR, (int64_t)kHC * H, 2),
-                       rows_span(post, M, kHC, kHC, 4),
-                       rows_span(comb, M, kHC * kHC, kHC * kHC, 4),
-                       Span{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)},
-                       Span{(uintptr_t)scale, (uintptr_t)scale + 12},
-                       Span{(uintptr_t)base, (uintptr_t)base + kMix * 4},
-                       Span{(uintptr_t)weight, (uintptr_t)weight + (uintptr_t)H * 2}};
-  const Span outs[6] = {rows_span(Rout, M, ldOut, (int64_t)kHC * H, 2), rows_span(y, M, ldY, H, 2),
-                        rows_span(post_out, M, kHC, kHC, 4),
-                        rows_span(comb_out, M, kHC * kHC, kHC * kHC, 4),
-                        Span{(uintptr_t)workspace, (uintptr_t)workspace + hc::stats_workspace_bytes(M)},
-                        pre_out ? rows_span(pre_out, M, kHC, kHC, 4) : Span{0, 0}};
-  for (int i = 0; i < 6; ++i) {
-    if (outs[i].b == outs[i].e) continue;
-    for (int j = 0; j < 8; ++j)
-      if (overlaps(outs[i], ins[j])) return HC_ERR_ALIAS;
-    for (int j = i + 1; j < 6; ++j)
-      if (outs[j].b != outs[j].e && overlaps(outs[i], outs[j])) return HC_ERR_ALIAS;
-  }
-  float* part = static_cast<float*>(workspace);
-  hipStream_t s = as_stream(stream);
-  if ((st = launched(hc::launch_post_stats(x, ldX, R, ldR, post, comb, fn_packed, (int)M, H, Rout,
-                                           ldOut, part, s))))
-    return st;
-  return launched(hc::launch_pre_finish(part, Rout, ldOut, scale, base, weight, (int)M, H, rms_eps,
-                                        pre_eps, sinkhorn_eps, iters, post_mult, norm_eps, y, ldY,
-                                        pre_out, post_out, comb_out, s));
+  const Finish f{scale, base, weight, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult, norm_eps,
+                 y, ldY, nullptr, 0, nullptr, 0, pre_out, post_out, comb_out};
+  return post_pre_impl(x, ldX, R, ldR, post, comb, fn_packed, M, H, Rout, ldOut, f, false,
+                       workspace, workspace_bytes, stream);
 }
 
+HC_API int hc_post_pre_mxfp8(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                             const float* post, const float* comb, const uint16_t* fn_packed,
+                             const float* scale, const float* base, const uint16_t* weight,
+                             int64_t M, int32_t H, float rms_eps, float pre_eps,
+                             float sinkhorn_eps, int32_t iters, float post_mult, float norm_eps,
+                             uint16_t* Rout, int64_t ldOut, uint16_t* y, int64_t ldY, uint8_t* q,
+                             int64_t ldQ, uint8_t* scales, int64_t ldS, float* pre_out,
+                             float* post_out, float* comb_out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  const Finish f{scale, base, weight, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult, norm_eps,
+                 y, ldY, q, ldQ, scales, ldS, pre_out, post_out, comb_out};
+  return post_pre_impl(x, ldX, R, ldR, post, comb, fn_packed, M, H, Rout, ldOut, f, true,
+                       workspace, workspace_bytes, stream);
+}
 
 // ---- the two halves of hc_post_pre ---------------------------------------------------------
 HC_API int hc_post_stats(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
@@ -328,24 +451,11 @@ HC_API int hc_post_stats(const uint16_t* x, int64_t ldX, const uint16_t* R, int6
   if (st) return st;
   if (!stats_h_ok(H) || !hc::combine_h_supported(H) || !post_h_ok(H)) return HC_ERR_SHAPE;
   if (M == 0) return HC_OK;
-  if (!x || !R || !post || !comb || !fn_packed || !Rout) return HC_ERR_NULL;
-  if ((st = check_residual(R, ldR, H))) return st;
-  if (ldX < H || ldOut < (int64_t)kHC * H) return HC_ERR_SHAPE;
-  if (!al16(x) || !al16(Rout) || !al16(post) || !al16(comb) || !al16(fn_packed) ||
-      (ldX * 2) % 16 || (ldOut * 2) % 16)
-    return HC_ERR_ALIGN;
-  if (!workspace || workspace_bytes < hc::stats_workspace_bytes(M)) return HC_ERR_WORKSPACE;
-  if (((uintptr_t)workspace & 255u) != 0) return HC_ERR_ALIGN;
-  const Span ins[5] = {rows_span(x, M, ldX, H, 2), rows_span(R, M, ldR, (int64_t)kHC * H, 2),
-                       rows_span(post, M, kHC, kHC, 4),
-                       rows_span(comb, M, kHC * kHC, kHC * kHC, 4),
-                       Span{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)}};
-  const Span outs[2] = {rows_span(Rout, M, ldOut, (int64_t)kHC * H, 2),
-                        Span{(uintptr_t)workspace, (uintptr_t)workspace + hc::stats_workspace_bytes(M)}};
-  if (overlaps(outs[0], outs[1])) return HC_ERR_ALIAS;
-  for (int i = 0; i < 2; ++i)
-    for (int j = 0; j < 5; ++j)
-      if (overlaps(outs[i], ins[j])) return HC_ERR_ALIAS;
+  Span ins[5], outs[2];
+  if ((st = post_stats_check(x, ldX, R, ldR, post, comb, fn_packed, M, H, Rout, ldOut, workspace,
+                             workspace_bytes, ins, outs)))
+    return st;
+  if ((st = no_alias(ins, 5, outs, 2))) return st;
   return launched(hc::launch_post_stats(x, ldX, R, ldR, post, comb, fn_packed, (int)M, H, Rout,
                                         ldOut, static_cast<float*>(workspace), as_stream(stream)));
 }
@@ -356,39 +466,42 @@ HC_API int hc_pre_finish(const uint16_t* R, int64_t ldR, const float* scale, con
                          float norm_eps, uint16_t* y, int64_t ldY, float* pre, float* post,
                          float* comb, const void* workspace, size_t workspace_bytes,
                          void* stream) {
+  const Finish f{scale, base, weight, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult, norm_eps,
+                 y, ldY, nullptr, 0, nullptr, 0, pre, post, comb};
+  return finish_impl(R, ldR, M, H, f, false, workspace, workspace_bytes, stream);
+}
+
+HC_API int hc_pre_finish_mxfp8(const uint16_t* R, int64_t ldR, const float* scale,
+                               const float* base, const uint16_t* weight, int64_t M, int32_t H,
+                               float rms_eps, float pre_eps, float sinkhorn_eps, int32_t iters,
+                               float post_mult, float norm_eps, uint16_t* y, int64_t ldY,
+                               uint8_t* q, int64_t ldQ, uint8_t* scales, int64_t ldS,
+                               float* pre, float* post, float* comb, const void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  const Finish f{scale, base, weight, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult, norm_eps,
+                 y, ldY, q, ldQ, scales, ldS, pre, post, comb};
+  return finish_impl(R, ldR, M, H, f, true, workspace, workspace_bytes, stream);
+}
+
+// ---- 128x4 scale layout ----------------------------------------------------------------------
+HC_API size_t mxfp8_swizzled_bytes(int64_t M, int32_t G) {
+  if (M < 0 || M >= kMaxRows || G <= 0 || G % 4 || G > (1 << 20)) return 0;
+  return (size_t)((M + 127) / 128) * 128 * (size_t)G;
+}
+
+HC_API int mxfp8_swizzle_128x4(const uint8_t* scales, int64_t ldS, int64_t M, int32_t G,
+                               uint8_t* out, void* stream) {
   int st = check_m(M);
   if (st) return st;
-  if (!stats_h_ok(H) || !hc::combine_h_supported(H)) return HC_ERR_SHAPE;
-  if (iters < 1 || iters > 100000) return HC_ERR_SHAPE;
-  if (!finite_nonneg(rms_eps) || !finite_nonneg(pre_eps) || !finite_nonneg(sinkhorn_eps) ||
-      !finite_nonneg(norm_eps) || !isfinite(post_mult))
-    return HC_ERR_ARG;
+  if (G <= 0 || G % 4 || G > (1 << 20)) return HC_ERR_SHAPE;
   if (M == 0) return HC_OK;
-  if (!R || !scale || !base || !weight || !y || !post || !comb) return HC_ERR_NULL;
-  if ((st = check_residual(R, ldR, H))) return st;
-  if (ldY < H) return HC_ERR_SHAPE;
-  if (!al16(weight) || !al16(y) || (ldY * 2) % 16) return HC_ERR_ALIGN;
-  if (!workspace || workspace_bytes < hc::stats_workspace_bytes(M)) return HC_ERR_WORKSPACE;
-  if (((uintptr_t)workspace & 255u) != 0) return HC_ERR_ALIGN;
-  const Span ins[5] = {rows_span(R, M, ldR, (int64_t)kHC * H, 2),
-                       Span{(uintptr_t)scale, (uintptr_t)scale + 12},
-                       Span{(uintptr_t)base, (uintptr_t)base + kMix * 4},
-                       Span{(uintptr_t)weight, (uintptr_t)weight + (uintptr_t)H * 2},
-                       Span{(uintptr_t)workspace, (uintptr_t)workspace + hc::stats_workspace_bytes(M)}};
-  const Span outs[4] = {rows_span(y, M, ldY, H, 2), rows_span(post, M, kHC, kHC, 4),
-                        rows_span(comb, M, kHC * kHC, kHC * kHC, 4),
-                        pre ? rows_span(pre, M, kHC, kHC, 4) : Span{0, 0}};
-  for (int i = 0; i < 4; ++i) {
-    if (outs[i].b == outs[i].e) continue;
-    for (int j = 0; j < 5; ++j)
-      if (overlaps(outs[i], ins[j])) return HC_ERR_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
-      if (outs[j].b != outs[j].e && overlaps(outs[i], outs[j])) return HC_ERR_ALIAS;
-  }
-  return launched(hc::launch_pre_finish(static_cast<const float*>(workspace), R, ldR, scale, base,
-                                        weight, (int)M, H, rms_eps, pre_eps, sinkhorn_eps, iters,
-                                        post_mult, norm_eps, y, ldY, pre, post, comb,
-                                        as_stream(stream)));
+  if (!scales || !out) return HC_ERR_NULL;
+  if (ldS < G) return HC_ERR_SHAPE;
+  if (((uintptr_t)out & 3u) != 0) return HC_ERR_ALIGN;
+  const Span in = rows_span(scales, M, ldS, G, 1);
+  const Span o{(uintptr_t)out, (uintptr_t)out + mxfp8_swizzled_bytes(M, G)};
+  if (overlaps(in, o)) return HC_ERR_ALIAS;
+  return launched(hc::launch_mx_swizzle(scales, ldS, (int)M, G, out, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -21,6 +21,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---- bf16 <-> fp32 -----------------------------------------------------------------------
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -88,6 +89,11 @@ __device__ __forceinline__ float quad_max(float v) {
   v = fmaxf(v, dpp<kQuadSwap2>(v));
   return v;
 }
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap2, 0xF, 0xF, false));
+  return v;
+}
 // Sum over the lanes {e, e+4, e+8, e+12} (mod 16) of each 16-lane group, lane e holding row
 // i = e / 4 of its column. Every lane forms ((v0 + v1) + (v2 + v3)) over the column's rows
 // (up to the order of the operands of each add, which does not change a rounded sum), so the
@@ -144,6 +150,60 @@ __device__ __forceinline__ float split_sinkhorn_lane(int e, float mix_a, float m
     p = p * __builtin_amdgcn_rcpf(stride4_sum(p) + sp.sk_eps);  // columns: sum over i
   }
   return p;
+}
+
+// ---- MXFP8 (OCP MX: e4m3fn elements, one ue8m0 scale per 32 values) -----------------------
+// Block exponent from the largest magnitude's bf16 bits (for finite bf16, magnitude order is
+// the integer order of the low 15 bits): the smallest e with amax * 2^-e <= 448 = 1.75 * 2^8.
+// With amax = (1 + f/128) * 2^(E-127), e = E - 135 + [f > 96] (1 + f/128 > 1.75 exactly when
+// f > 96), clamped to [-127, 127]; zero and bf16-subnormal maxima give -127. The scale byte
+// is e + 127.
+__device__ __forceinline__ int mx_block_exponent(uint32_t amax_bits) {
+  const int E = (int)(amax_bits >> 7);
+  const int f = (int)(amax_bits & 0x7f);
+  const int e = (E == 0) ? -127 : E - 135 + (f > 96 ? 1 : 0);
+  return min(max(e, -127), 127);
+}
+
+// 2^-e as fp32, exact for e in [-127, 126] (finite bf16 maxima give e <= 120).
+__device__ __forceinline__ float mx_inv_scale(int e) {
+  return __uint_as_float((uint32_t)(127 - e) << 23);
+}
+
+// fp32 -> e4m3fn code, round to nearest even, saturating to +-448 (0x7E / 0xFE), sign of zero
+// kept. Exponent bias 7, 3 mantissa bits; below 2^-6 the codes are multiples of 2^-9.
+__device__ __forceinline__ uint32_t e4m3_code(float s) {
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t code;
+  if (a >= 0x3C800000u) {  // |s| >= 2^-6: normal e4m3 after rounding
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);  // round to 3 mantissa bits, ties even
+    const int ex = (int)(r >> 23) - 127 + 7;
+    const uint32_t man = (r >> 20) & 7u;
+    code = (ex > 15 || (ex == 15 && man == 7u)) ? 0x7Eu : (((uint32_t)ex << 3) | man);
+  } else {  // subnormal range: multiples of 2^-9, rounded to nearest even
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  return code | sign;
+}
+
+// Four bf16 values in two packed words, w0 = (v0, v1) and w1 = (v2, v3), scaled by inv
+// -> four e4m3 codes in one word, v0 in the low byte.
+__device__ __forceinline__ uint32_t e4m3_word(uint32_t w0, uint32_t w1, float inv) {
+  return e4m3_code(bf_lo(w0) * inv) | (e4m3_code(bf_hi(w0) * inv) << 8) |
+         (e4m3_code(bf_lo(w1) * inv) << 16) | (e4m3_code(bf_hi(w1) * inv) << 24);
+}
+
+// Largest magnitude bits (low 15 bits) of 8 packed bf16.
+__device__ __forceinline__ uint32_t amax_bits8(const u32x4& w) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = max(m, w[i] & 0x7fffu);
+    m = max(m, (w[i] >> 16) & 0x7fffu);
+  }
+  return m;
 }
 
 // mixes[f] = d[f] * rsqrt(sumsq / K + eps): the scale factor of the mix stats

@@ -57,11 +57,15 @@ hipError_t launch_sinkhorn(const float* mixes, int M, const float* scale, const 
 hipError_t launch_combine_norm(const uint16_t* R, int64_t ldR, const float* pre, int64_t ldPre,
                                const uint16_t* w, int M, int H, float eps, uint16_t* y,
                                int64_t ldY, hipStream_t s);
+// q == NULL: bf16 y only; otherwise also (or, with y == NULL, only) the MXFP8 form of y
 hipError_t launch_pre_finish(const float* part, const uint16_t* R, int64_t ldR,
                              const float* scale, const float* base, const uint16_t* w, int M,
                              int H, float rms_eps, float pre_eps, float sk_eps, int iters,
                              float post_mult, float norm_eps, uint16_t* y, int64_t ldY,
-                             float* pre, float* post, float* comb, hipStream_t s);
+                             uint8_t* q, int64_t ldQ, uint8_t* sc, int64_t ldS, float* pre,
+                             float* post, float* comb, hipStream_t s);
+hipError_t launch_mx_swizzle(const uint8_t* sc, int64_t ldS, int M, int G, uint8_t* out,
+                             hipStream_t s);
 
 hipError_t launch_post(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
                        const float* post, const float* comb, int M, int H, uint16_t* out,

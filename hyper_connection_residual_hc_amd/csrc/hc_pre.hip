@@ -81,10 +81,14 @@ __device__ __forceinline__ void load_row(const uint16_t* __restrict__ Rr,
   }
 }
 
-template <int NG>
+// y's row: written as bf16 when yr is given, and with kMx also as MXFP8 (qr: e4m3 codes,
+// sr: one scale byte per 32 columns) quantised from the same bf16 values, with the rule of
+// mxfp8_quant_rows. A 32-column block is the 8 columns of each lane of a lane quad.
+template <int NG, bool kMx>
 __device__ __forceinline__ void combine_norm_row(const RowTile<NG>& t, const float (&p)[kHC],
                                                  const uint16_t* __restrict__ w, float eps,
-                                                 uint16_t* __restrict__ yr, int lane) {
+                                                 uint16_t* __restrict__ yr, uint8_t* __restrict__ qr,
+                                                 uint8_t* __restrict__ sr, int lane) {
   constexpr int H = NG * 512;
   float c[NG][8];
   float ss = 0.0f;
@@ -113,7 +117,17 @@ __device__ __forceinline__ void combine_norm_row(const RowTile<NG>& t, const flo
       unpack8(ld16(w + g * 512 + lane * 8), wf);
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (c[g][e] * rn) * wf[e];
-    st16(yr + g * 512 + lane * 8, pack8(o));
+    const u32x4 yb = pack8(o);
+    if (!kMx || yr) st16(yr + g * 512 + lane * 8, yb);
+    if constexpr (kMx) {
+      const int ex = mx_block_exponent(quad_max_u32(amax_bits8(yb)));
+      const float inv = mx_inv_scale(ex);
+      u32x2 codes;
+      codes[0] = e4m3_word(yb[0], yb[1], inv);
+      codes[1] = e4m3_word(yb[2], yb[3], inv);
+      *reinterpret_cast<u32x2*>(qr + g * 512 + lane * 8) = codes;
+      if ((lane & 3) == 0) sr[g * 16 + (lane >> 2)] = (uint8_t)(ex + 127);
+    }
   }
 }
 
@@ -134,16 +148,17 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const uint16_t* __res
   float p[kHC];
 #pragma unroll
   for (int i = 0; i < kHC; ++i) p[i] = pre[(int64_t)m * ldPre + i];
-  combine_norm_row<NG>(t, p, w, eps, y + (int64_t)m * ldY, lane);
+  combine_norm_row<NG, false>(t, p, w, eps, y + (int64_t)m * ldY, nullptr, nullptr, lane);
 }
 
 // ---- fused: slice reduce + split + Sinkhorn + combine + RMSNorm ----------------------------
-template <int NG>
+template <int NG, bool kMx>
 __global__ __launch_bounds__(256) void pre_finish_kernel(
     const float* __restrict__ part, const uint16_t* __restrict__ R, int64_t ldR,
     const float* __restrict__ scale, const float* __restrict__ base,
     const uint16_t* __restrict__ w, int M, float kf, float rms_eps, float pre_eps, float sk_eps,
     int iters, float post_mult, float norm_eps, uint16_t* __restrict__ y, int64_t ldY,
+    uint8_t* __restrict__ q, int64_t ldQ, uint8_t* __restrict__ sc, int64_t ldS,
     float* __restrict__ pre, float* __restrict__ post, float* __restrict__ comb) {
   const int lane = threadIdx.x & 63;
   const int m = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
@@ -183,7 +198,9 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(
   float p[kHC];
 #pragma unroll
   for (int i = 0; i < kHC; ++i) p[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), i));
-  combine_norm_row<NG>(t, p, w, norm_eps, y + (int64_t)m * ldY, lane);
+  combine_norm_row<NG, kMx>(t, p, w, norm_eps, y ? y + (int64_t)m * ldY : nullptr,
+                            kMx ? q + (int64_t)m * ldQ : nullptr,
+                            kMx ? sc + (int64_t)m * ldS : nullptr, lane);
 }
 
 // ---- dispatch over the compiled H values ----------------------------------------------------
@@ -220,15 +237,21 @@ hipError_t launch_pre_finish(const float* part, const uint16_t* R, int64_t ldR,
                              const float* scale, const float* base, const uint16_t* w, int M,
                              int H, float rms_eps, float pre_eps, float sk_eps, int iters,
                              float post_mult, float norm_eps, uint16_t* y, int64_t ldY,
-                             float* pre, float* post, float* comb, hipStream_t s) {
+                             uint8_t* q, int64_t ldQ, uint8_t* sc, int64_t ldS, float* pre,
+                             float* post, float* comb, hipStream_t s) {
   const dim3 grid((unsigned)((M + 3) / 4)), block(256);
   const float kf = (float)(4 * H);
   switch (H / 512) {
 #define HC_CASE(n)                                                                              \
   case n:                                                                                       \
-    hipLaunchKernelGGL(pre_finish_kernel<n>, grid, block, 0, s, part, R, ldR, scale, base, w,   \
-                       M, kf, rms_eps, pre_eps, sk_eps, iters, post_mult, norm_eps, y, ldY,    \
-                       pre, post, comb);                                                        \
+    if (q)                                                                                      \
+      hipLaunchKernelGGL((pre_finish_kernel<n, true>), grid, block, 0, s, part, R, ldR, scale,  \
+                         base, w, M, kf, rms_eps, pre_eps, sk_eps, iters, post_mult, norm_eps,  \
+                         y, ldY, q, ldQ, sc, ldS, pre, post, comb);                             \
+    else                                                                                        \
+      hipLaunchKernelGGL((pre_finish_kernel<n, false>), grid, block, 0, s, part, R, ldR, scale, \
+                         base, w, M, kf, rms_eps, pre_eps, sk_eps, iters, post_mult, norm_eps,  \
+                         y, ldY, q, ldQ, sc, ldS, pre, post, comb);                             \
     break;
     HC_FOR_EACH_NG(HC_CASE)
 #undef HC_CASE

@@ -339,3 +339,118 @@ def pre_finish(R: torch.Tensor, workspace: torch.Tensor, scale: torch.Tensor,
               comb_o.data_ptr(), workspace.data_ptr(),
               workspace.numel() * workspace.element_size(), _stream(R))
     return y, post_o, comb_o, pre_o
+
+
+# ---- MXFP8 output of the pre ------------------------------------------------------------------
+def _mx_outputs(M: int, H: int, dev, want_y: bool, want_pre: bool, out):
+    """(y or None, q, scales, post, comb, pre or None), allocated unless given, then checked."""
+    if out is None:
+        out = (torch.empty(M, H, dtype=torch.bfloat16, device=dev) if want_y else None,
+               torch.empty(M, H, dtype=torch.uint8, device=dev),
+               torch.empty(M, H // 32, dtype=torch.uint8, device=dev),
+               torch.empty(M, HC, dtype=torch.float32, device=dev),
+               torch.empty(M, HC, HC, dtype=torch.float32, device=dev),
+               torch.empty(M, HC, dtype=torch.float32, device=dev) if want_pre else None)
+    y, q, sc, post_o, comb_o, pre_o = out
+    if y is not None:
+        _shaped(y, "y", torch.bfloat16, (M, H))
+    _shaped(q, "q", torch.uint8, (M, H))
+    _shaped(sc, "scales", torch.uint8, (M, H // 32))
+    _contig(post_o, "post", torch.float32, (M, HC))
+    _contig(comb_o, "comb", torch.float32, (M, HC, HC))
+    if pre_o is not None:
+        _contig(pre_o, "pre", torch.float32, (M, HC))
+    return out
+
+
+def _mx_args(out, H):
+    y, q, sc, post_o, comb_o, pre_o = out
+    return (_ptr(y), _rows(y, H) if y is not None else H, q.data_ptr(), _rows(q, H),
+            sc.data_ptr(), _rows(sc, H // 32), _ptr(pre_o), post_o.data_ptr(), comb_o.data_ptr())
+
+
+def pre_mxfp8(R: torch.Tensor, fn_packed: torch.Tensor, scale: torch.Tensor, base: torch.Tensor,
+              weight: torch.Tensor, rms_eps: float = RMS_EPS, pre_eps: float = HC_EPS,
+              sinkhorn_eps: float = HC_EPS, iters: int = ITERS, post_mult: float = POST_MULT,
+              norm_eps: float = RMS_EPS, want_y: bool = True, want_pre: bool = False, out=None,
+              workspace: Optional[torch.Tensor] = None):
+    """hc_pre with y also in MXFP8: (y bf16 or None, q u8 [M, H], scales u8 [M, H/32] linear,
+    post, comb, pre or None)."""
+    M, H, ldR = _residual(R)
+    _packed(fn_packed, H)
+    _contig(scale, "scale", torch.float32, (3,))
+    _contig(base, "base", torch.float32, (MIX,))
+    _contig(weight, "weight", torch.bfloat16, (H,))
+    out = _mx_outputs(M, H, R.device, want_y, want_pre, out)
+    ws = _workspace(pre_workspace_bytes(M, H), R.device, workspace)
+    _lib.call("hc_pre_mxfp8", R.data_ptr(), ldR, fn_packed.data_ptr(), scale.data_ptr(),
+              base.data_ptr(), weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters,
+              post_mult, norm_eps, *_mx_args(out, H), ws.data_ptr(),
+              ws.numel() * ws.element_size(), _stream(R))
+    return out
+
+
+def post_pre_mxfp8(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.Tensor,
+                   fn_packed: torch.Tensor, scale: torch.Tensor, base: torch.Tensor,
+                   weight: torch.Tensor, rms_eps: float = RMS_EPS, pre_eps: float = HC_EPS,
+                   sinkhorn_eps: float = HC_EPS, iters: int = ITERS,
+                   post_mult: float = POST_MULT, norm_eps: float = RMS_EPS,
+                   want_y: bool = True, want_pre: bool = False, R_out=None, out=None,
+                   workspace: Optional[torch.Tensor] = None):
+    """hc_post_pre with y also in MXFP8: (R', (y or None, q, scales, post', comb', pre' or None))."""
+    M, H, ldR = _residual(R)
+    _need(x, "x", torch.bfloat16, 2)
+    if tuple(x.shape) != (M, H):
+        raise ValueError(f"x must be [{M}, {H}]")
+    _contig(post_, "post", torch.float32, (M, HC))
+    _contig(comb, "comb", torch.float32, (M, HC, HC))
+    _packed(fn_packed, H)
+    _contig(scale, "scale", torch.float32, (3,))
+    _contig(base, "base", torch.float32, (MIX,))
+    _contig(weight, "weight", torch.bfloat16, (H,))
+    if R_out is None:
+        R_out = torch.empty(M, HC, H, dtype=torch.bfloat16, device=R.device)
+    _shaped(R_out, "R_out", torch.bfloat16, (M, HC, H))
+    _, _, ldOut = _residual(R_out)
+    out = _mx_outputs(M, H, R.device, want_y, want_pre, out)
+    ws = _workspace(post_pre_workspace_bytes(M, H), R.device, workspace)
+    _lib.call("hc_post_pre_mxfp8", x.data_ptr(), _rows(x, H), R.data_ptr(), ldR,
+              post_.data_ptr(), comb.data_ptr(), fn_packed.data_ptr(), scale.data_ptr(),
+              base.data_ptr(), weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters,
+              post_mult, norm_eps, R_out.data_ptr(), ldOut, *_mx_args(out, H), ws.data_ptr(),
+              ws.numel() * ws.element_size(), _stream(R))
+    return R_out, out
+
+
+def pre_finish_mxfp8(R: torch.Tensor, workspace: torch.Tensor, scale: torch.Tensor,
+                     base: torch.Tensor, weight: torch.Tensor, rms_eps: float = RMS_EPS,
+                     pre_eps: float = HC_EPS, sinkhorn_eps: float = HC_EPS, iters: int = ITERS,
+                     post_mult: float = POST_MULT, norm_eps: float = RMS_EPS,
+                     want_y: bool = True, want_pre: bool = False, out=None):
+    """Second half of post_pre_mxfp8, on post_stats's (R', workspace)."""
+    M, H, ldR = _residual(R)
+    _contig(scale, "scale", torch.float32, (3,))
+    _contig(base, "base", torch.float32, (MIX,))
+    _contig(weight, "weight", torch.bfloat16, (H,))
+    out = _mx_outputs(M, H, R.device, want_y, want_pre, out)
+    _lib.call("hc_pre_finish_mxfp8", R.data_ptr(), ldR, scale.data_ptr(), base.data_ptr(),
+              weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult,
+              norm_eps, *_mx_args(out, H), workspace.data_ptr(),
+              workspace.numel() * workspace.element_size(), _stream(R))
+    return out
+
+
+def mxfp8_swizzle_128x4(scales: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Linear ue8m0 scales [M, G] -> the 128x4 tiled layout, flat uint8 of
+    ceil(M / 128) * 128 * G bytes (padded rows zero)."""
+    _need(scales, "scales", torch.uint8, 2)
+    M, G = scales.shape
+    nbytes = int(_lib.lib().mxfp8_swizzled_bytes(M, G))
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=scales.device)
+    _shaped(out, "out", torch.uint8, (nbytes,))
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    _lib.call("mxfp8_swizzle_128x4", scales.data_ptr(), _rows(scales, G), M, G, out.data_ptr(),
+              _stream(scales))
+    return out

@@ -18,7 +18,8 @@
  * - M == 0 is a successful no-op. A row slice [a, b) of a call is the same call with every
  *   row pointer advanced by a rows and M = b - a; the library takes no "logical row count"
  *   and keys no choice on M, and every row's result is bit-identical whether the row is
- *   computed in a full call or in any slice.
+ *   computed in a full call or in any slice (mxfp8_swizzle_128x4, a layout over the whole
+ *   of M, is the one exception).
  * - Return value: HC_OK (0) or one of the HC_ERR_* codes below; hc_status_string() names it.
  *   An error return means nothing was enqueued.
  *
@@ -218,6 +219,56 @@ HC_API int hc_pre_finish(const uint16_t* R, int64_t ldR, const float* scale, con
                          float norm_eps, uint16_t* y, int64_t ldY, float* pre, float* post,
                          float* comb, const void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * MXFP8 output of the pre (prefill_sp.py, module docstring stage 2: the attention input is
+ * all-gathered as e4m3 bytes plus ue8m0 scales; _mxfp8_quantize / mxfp8_gather quantise each
+ * row shard with linear scales). These are hc_pre, hc_post_pre and hc_pre_finish with the
+ * normalised input y also written in MXFP8, quantised inside the same pass from the same bf16
+ * values: q / scales are bit-identical to mxfp8_quant_rows of the y the bf16 form writes.
+ *
+ * y: bf16 [M, H] (ldY), or NULL to skip the bf16 form. q: u8 [M, H] e4m3fn codes (ldQ >= H,
+ * ldQ % 16 == 0, 16-byte aligned). scales: u8 [M, H/32] linear (ldS >= H/32, any alignment).
+ * Every other argument, and the error behaviour, as in the bf16 entry point of the same name.
+ * ------------------------------------------------------------------------------------- */
+HC_API int hc_pre_mxfp8(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed,
+                        const float* scale, const float* base, const uint16_t* weight, int64_t M,
+                        int32_t H, float rms_eps, float pre_eps, float sinkhorn_eps,
+                        int32_t iters, float post_mult, float norm_eps, uint16_t* y, int64_t ldY,
+                        uint8_t* q, int64_t ldQ, uint8_t* scales, int64_t ldS, float* pre,
+                        float* post, float* comb, void* workspace, size_t workspace_bytes,
+                        void* stream);
+HC_API int hc_post_pre_mxfp8(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                             const float* post, const float* comb, const uint16_t* fn_packed,
+                             const float* scale, const float* base, const uint16_t* weight,
+                             int64_t M, int32_t H, float rms_eps, float pre_eps,
+                             float sinkhorn_eps, int32_t iters, float post_mult, float norm_eps,
+                             uint16_t* Rout, int64_t ldOut, uint16_t* y, int64_t ldY, uint8_t* q,
+                             int64_t ldQ, uint8_t* scales, int64_t ldS, float* pre_out,
+                             float* post_out, float* comb_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+HC_API int hc_pre_finish_mxfp8(const uint16_t* R, int64_t ldR, const float* scale,
+                               const float* base, const uint16_t* weight, int64_t M, int32_t H,
+                               float rms_eps, float pre_eps, float sinkhorn_eps, int32_t iters,
+                               float post_mult, float norm_eps, uint16_t* y, int64_t ldY,
+                               uint8_t* q, int64_t ldQ, uint8_t* scales, int64_t ldS,
+                               float* pre, float* post, float* comb, const void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * 128x4 scale layout (prefill_sp.py, swizzle_128x4: what the attention GEMM takes after the
+ * gather). From linear scales [M, G]: rows are zero-padded to a multiple of 128; 128 x 4
+ * tiles (m / 128, g / 4) follow in row-tile-major order, 512 bytes each; inside a tile the
+ * scale of (m, g) sits at byte (m % 32) * 16 + ((m % 128) / 32) * 4 + g % 4.
+ *
+ * scales: u8 [M, G] with row stride ldS >= G (device). out: mxfp8_swizzled_bytes(M, G) bytes
+ * (device, 4-byte aligned), every byte written. G: multiple of 4 (H / 32 for H % 128 == 0).
+ * The layout is over the whole of M: unlike the other entry points, a row slice of a call is
+ * not a call on a slice (swizzle the gathered scales, as the pages do).
+ * ------------------------------------------------------------------------------------- */
+HC_API size_t mxfp8_swizzled_bytes(int64_t M, int32_t G);
+HC_API int mxfp8_swizzle_128x4(const uint8_t* scales, int64_t ldS, int64_t M, int32_t G,
+                               uint8_t* out, void* stream);
 
 #ifdef __cplusplus
 }

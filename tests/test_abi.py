@@ -106,3 +106,28 @@ def test_validation_codes_of_the_post_pre_halves(L):
     # the workspace is an input of the second half: y over it is an alias
     assert L.hc_pre_finish(a, 4 * H, b, c, d, 7, H, 1e-6, 1e-6, 1e-6, 20, 2.0, 1e-6, ws, H,
                            None, fake, ctypes.c_void_p(0x6000000), ws, need, None) == 4
+
+
+def test_mxfp8_epilogue_and_swizzle_checks(L):
+    H = 5120
+    assert L.mxfp8_swizzled_bytes(130, 160) == 256 * 160
+    assert L.mxfp8_swizzled_bytes(128, 160) == 128 * 160
+    assert L.mxfp8_swizzled_bytes(0, 160) == 0
+    assert L.mxfp8_swizzled_bytes(5, 6) == 0  # G must be a multiple of 4
+    a, b = ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000)
+    assert L.mxfp8_swizzle_128x4(a, 160, 5, 6, b, None) == 2
+    assert L.mxfp8_swizzle_128x4(a, 100, 5, 160, b, None) == 2  # ldS < G
+    assert L.mxfp8_swizzle_128x4(a, 160, 5, 160, ctypes.c_void_p(0x2000002), None) == 3
+    assert L.mxfp8_swizzle_128x4(a, 160, 5, 160, ctypes.c_void_p(0x1000010), None) == 4
+    assert L.mxfp8_swizzle_128x4(None, 160, 0, 160, None, None) == 0
+    # hc_pre_mxfp8: q is required, y is not; q row stride must keep 16-byte rows
+    fake = ctypes.c_void_p(0x10000)
+    ws = ctypes.c_void_p(0x5000000)
+    need = L.hc_pre_workspace_bytes(7, H)
+    args = [a, 4 * H, fake, fake, fake, fake, 7, H, 1e-6, 1e-6, 1e-6, 20, 2.0, 1e-6]
+    assert L.hc_pre_mxfp8(*args, None, H, None, H, fake, H // 32, None, fake, fake, ws, need,
+                          None) == 1
+    assert L.hc_pre_mxfp8(*args, None, H, b, H + 8, fake, H // 32, None, fake, fake, ws, need,
+                          None) == 3
+    assert L.hc_pre_mxfp8(*args, None, H, b, H - 16, fake, H // 32, None, fake, fake, ws, need,
+                          None) == 2
