@@ -52,6 +52,9 @@ SIGNATURES = {
                                    _f32, _f32, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _p, _sz,
                                    _p]),
     "mxfp8_swizzled_bytes": (_sz, [_i64, _i32]),
+    "hc_head_fn_pack": (_int, [_p, _i32, _p, _p]),
+    "hc_head_workspace_bytes": (_sz, [_i64, _i32]),
+    "hc_head": (_int, [_p, _i64, _p, _p, _p, _i64, _i32, _f32, _f32, _p, _i64, _p, _sz, _p]),
     "mxfp8_swizzle_128x4": (_int, [_p, _i64, _i64, _i32, _p, _p]),
 }
 

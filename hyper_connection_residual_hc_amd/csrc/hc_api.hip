@@ -252,7 +252,17 @@ HC_API int hc_fn_pack(const float* fn, int32_t H, uint16_t* fn_packed, void* str
   const Span in{(uintptr_t)fn, (uintptr_t)fn + (uintptr_t)kMix * 4 * H * 4};
   const Span out{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)};
   if (overlaps(in, out)) return HC_ERR_ALIAS;
-  return launched(hc::launch_fn_pack(fn, H, fn_packed, as_stream(stream)));
+  return launched(hc::launch_fn_pack(fn, H, kMix, fn_packed, as_stream(stream)));
+}
+
+HC_API int hc_head_fn_pack(const float* fn, int32_t H, uint16_t* fn_packed, void* stream) {
+  if (!stats_h_ok(H)) return HC_ERR_SHAPE;
+  if (!fn || !fn_packed) return HC_ERR_NULL;
+  if (!al16(fn_packed)) return HC_ERR_ALIGN;
+  const Span in{(uintptr_t)fn, (uintptr_t)fn + (uintptr_t)kHC * 4 * H * 4};
+  const Span out{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)};
+  if (overlaps(in, out)) return HC_ERR_ALIAS;
+  return launched(hc::launch_fn_pack(fn, H, kHC, fn_packed, as_stream(stream)));
 }
 
 // ---- stage 1 -----------------------------------------------------------------------------
@@ -481,6 +491,38 @@ HC_API int hc_pre_finish_mxfp8(const uint16_t* R, int64_t ldR, const float* scal
   const Finish f{scale, base, weight, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult, norm_eps,
                  y, ldY, q, ldQ, scales, ldS, pre, post, comb};
   return finish_impl(R, ldR, M, H, f, true, workspace, workspace_bytes, stream);
+}
+
+// ---- hc_head ---------------------------------------------------------------------------------
+HC_API size_t hc_head_workspace_bytes(int64_t M, int32_t H) {
+  return hc_pre_stats_workspace_bytes(M, H);
+}
+
+HC_API int hc_head(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, const float* scale,
+                   const float* base, int64_t M, int32_t H, float norm_eps, float hc_eps,
+                   uint16_t* y, int64_t ldY, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if (!stats_h_ok(H) || !hc::combine_h_supported(H)) return HC_ERR_SHAPE;
+  if (!finite_nonneg(norm_eps) || !isfinite(hc_eps)) return HC_ERR_ARG;
+  if (M == 0) return HC_OK;
+  if (!R || !fn_packed || !scale || !base || !y) return HC_ERR_NULL;
+  if ((st = check_residual(R, ldR, H))) return st;
+  if (ldY < H) return HC_ERR_SHAPE;
+  if (!al16(fn_packed) || !al16(y) || (ldY * 2) % 16) return HC_ERR_ALIGN;
+  if ((st = workspace_ok(workspace, workspace_bytes, M))) return st;
+  const Span ins[4] = {rows_span(R, M, ldR, (int64_t)kHC * H, 2),
+                       Span{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)},
+                       Span{(uintptr_t)scale, (uintptr_t)scale + 4},
+                       Span{(uintptr_t)base, (uintptr_t)base + kHC * 4}};
+  const Span outs[2] = {rows_span(y, M, ldY, H, 2), workspace_span(workspace, M)};
+  if ((st = no_alias(ins, 4, outs, 2))) return st;
+  float* part = static_cast<float*>(workspace);
+  hipStream_t s = as_stream(stream);
+  if ((st = launched(hc::launch_stats(R, ldR, fn_packed, (int)M, H, part, s)))) return st;
+  return launched(hc::launch_head_finish(part, R, ldR, scale, base, (int)M, H, norm_eps, hc_eps,
+                                         y, ldY, s));
 }
 
 // ---- 128x4 scale layout ----------------------------------------------------------------------

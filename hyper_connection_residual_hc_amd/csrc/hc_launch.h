@@ -40,7 +40,8 @@ __device__ __forceinline__ float slice_sum(const float* __restrict__ part, int M
   return slice_sum(v);
 }
 
-hipError_t launch_fn_pack(const float* fn, int H, uint16_t* fn_packed, hipStream_t s);
+// fn [rows, 4H] (rows <= 24) into the packed stats operands; missing rows are zero
+hipError_t launch_fn_pack(const float* fn, int H, int rows, uint16_t* fn_packed, hipStream_t s);
 hipError_t launch_stats(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, int M, int H,
                         float* part, hipStream_t s);
 hipError_t launch_stats_reduce(const float* part, int M, int H, float rms_eps, float* mixes,
@@ -64,6 +65,12 @@ hipError_t launch_pre_finish(const float* part, const uint16_t* R, int64_t ldR,
                              float post_mult, float norm_eps, uint16_t* y, int64_t ldY,
                              uint8_t* q, int64_t ldQ, uint8_t* sc, int64_t ldS, float* pre,
                              float* post, float* comb, hipStream_t s);
+// hc_head from the stats partials: pre = sigmoid(mixes[0..3] * scale[0] + base) + hc_eps,
+// y = bf16(sum_i pre_i R_i)
+hipError_t launch_head_finish(const float* part, const uint16_t* R, int64_t ldR,
+                              const float* scale, const float* base, int M, int H,
+                              float norm_eps, float hc_eps, uint16_t* y, int64_t ldY,
+                              hipStream_t s);
 hipError_t launch_mx_swizzle(const uint8_t* sc, int64_t ldS, int M, int G, uint8_t* out,
                              hipStream_t s);
 

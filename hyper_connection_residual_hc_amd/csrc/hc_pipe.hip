@@ -76,8 +76,9 @@ __device__ __forceinline__ int64_t chunk_col0(int s, int c, int H) {
   return (int64_t)j * H + (int64_t)s * (H / kSlices) + 64 * p + 32 * hq;
 }
 
+// fn has `rows` rows (24 for the mixes, 4 for the head); rows past it pack as zeros.
 __global__ __launch_bounds__(256) void fn_pack_kernel(const float* __restrict__ fn, int H,
-                                                      uint16_t* __restrict__ out) {
+                                                      int rows, uint16_t* __restrict__ out) {
   const int NCS = (int)chunks_per_slice(H);
   const int64_t total = (int64_t)kSlices * NCS * kPackTiles * 64;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(256) void fn_pack_kernel(const float* __restrict__ 
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float val = 0.0f;
-    if (f >= 0) {
+    if (f >= 0 && f < rows) {
       const float a = fn[(int64_t)f * 4 * H + k + e];
       const float hi = bf16_round(a);
       const float r1 = a - hi;  // exact
@@ -109,10 +110,11 @@ __global__ __launch_bounds__(256) void fn_pack_kernel(const float* __restrict__ 
   st16(out + gid * 8, pack8(v));  // the parts are exact bf16 values: packing does not round
 }
 
-hipError_t launch_fn_pack(const float* fn, int H, uint16_t* fn_packed, hipStream_t s) {
+hipError_t launch_fn_pack(const float* fn, int H, int rows, uint16_t* fn_packed,
+                          hipStream_t s) {
   const int64_t total = (int64_t)kSlices * chunks_per_slice(H) * kPackTiles * 64;
   hipLaunchKernelGGL(fn_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, fn,
-                     H, fn_packed);
+                     H, rows, fn_packed);
   return hipGetLastError();
 }
 

@@ -66,7 +66,7 @@ struct RowTile {
 
 // The row (streamed once, non-temporal), then the weight (shared by every row: cached). All
 // loads go out together so their latencies overlap.
-template <int NG>
+template <int NG, bool kWeight = true>
 __device__ __forceinline__ void load_row(const uint16_t* __restrict__ Rr,
                                          const uint16_t* __restrict__ w, int lane,
                                          RowTile<NG>& t) {
@@ -75,7 +75,7 @@ __device__ __forceinline__ void load_row(const uint16_t* __restrict__ Rr,
   for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int i = 0; i < kHC; ++i) t.r[g][i] = ld16_stream(Rr + i * H + g * 512 + lane * 8);
-  if constexpr (kPreloadWeight<NG>) {
+  if constexpr (kWeight && kPreloadWeight<NG>) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) t.w[g] = ld16(w + g * 512 + lane * 8);
   }
@@ -203,6 +203,51 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(
                             kMx ? sc + (int64_t)m * ldS : nullptr, lane);
 }
 
+// ---- hc_head: the model's last mix (deepseek_v4.py, hc_head_torch / fused_hc_head) -----------
+// From the slice partials of a 4-row fn (packed as rows 0..3 of the 24-row layout):
+//   mixes[i] = d[i] * rsqrt(sum x^2 / 4H + norm_eps),  pre_i = sigmoid(mixes[i] * scale + base_i)
+//   + hc_eps,  y = bf16(sum_i pre_i R_i) (fp32, one rounding; no norm: the model's final
+// RMSNorm follows separately). One wave per row; every lane forms the four pre values.
+template <int NG>
+__global__ __launch_bounds__(256) void head_finish_kernel(
+    const float* __restrict__ part, const uint16_t* __restrict__ R, int64_t ldR,
+    const float* __restrict__ scale, const float* __restrict__ base, int M, float kf,
+    float norm_eps, float hc_eps, uint16_t* __restrict__ y, int64_t ldY) {
+  constexpr int H = NG * 512;
+  const int lane = threadIdx.x & 63;
+  const int m = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
+  if (m >= M) return;
+  float pd[kHC][kSlices], pq[kSlices];
+#pragma unroll
+  for (int i = 0; i < kHC; ++i) slice_load(part, M, m, i, pd[i]);
+  slice_load(part, M, m, kMix, pq);
+  __builtin_amdgcn_sched_barrier(0);
+  RowTile<NG> t;
+  load_row<NG, false>(R + (int64_t)m * ldR, nullptr, lane, t);
+  __builtin_amdgcn_sched_barrier(0);
+  const float rs = mix_rscale(slice_sum(pq), kf, norm_eps);
+  const float s0 = scale[0];
+  float p[kHC];
+#pragma unroll
+  for (int i = 0; i < kHC; ++i) p[i] = sigmoidf_(__fmaf_rn(slice_sum(pd[i]) * rs, s0, base[i])) + hc_eps;
+  uint16_t* yr = y + (int64_t)m * ldY;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float r[kHC][8], o[8];
+#pragma unroll
+    for (int i = 0; i < kHC; ++i) unpack8(t.r[g][i], r[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = p[0] * r[0][e];
+#pragma unroll
+      for (int i = 1; i < kHC; ++i) a = __fmaf_rn(p[i], r[i][e], a);
+      o[e] = a;
+    }
+    st16(yr + g * 512 + lane * 8, pack8(o));
+  }
+  (void)H;
+}
+
 // ---- dispatch over the compiled H values ----------------------------------------------------
 #define HC_FOR_EACH_NG(X) X(1) X(2) X(4) X(8) X(10) X(14) X(16)
 
@@ -252,6 +297,25 @@ hipError_t launch_pre_finish(const float* part, const uint16_t* R, int64_t ldR,
       hipLaunchKernelGGL((pre_finish_kernel<n, false>), grid, block, 0, s, part, R, ldR, scale, \
                          base, w, M, kf, rms_eps, pre_eps, sk_eps, iters, post_mult, norm_eps,  \
                          y, ldY, q, ldQ, sc, ldS, pre, post, comb);                             \
+    break;
+    HC_FOR_EACH_NG(HC_CASE)
+#undef HC_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_head_finish(const float* part, const uint16_t* R, int64_t ldR,
+                              const float* scale, const float* base, int M, int H,
+                              float norm_eps, float hc_eps, uint16_t* y, int64_t ldY,
+                              hipStream_t s) {
+  const dim3 grid((unsigned)((M + 3) / 4)), block(256);
+  const float kf = (float)(4 * H);
+  switch (H / 512) {
+#define HC_CASE(n)                                                                              \
+  case n:                                                                                       \
+    hipLaunchKernelGGL(head_finish_kernel<n>, grid, block, 0, s, part, R, ldR, scale, base, M,  \
+                       kf, norm_eps, hc_eps, y, ldY);                                           \
     break;
     HC_FOR_EACH_NG(HC_CASE)
 #undef HC_CASE

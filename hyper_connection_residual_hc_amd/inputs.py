@@ -17,7 +17,8 @@ Distributions follow the one-GPU test page of the prefill sequence-parallel adap
 
 Parameter tensors for one site are drawn from one generator in the order fn, base, scale,
 as the test page does. Seeds: attention-site parameters 11, FFN-site parameters 61 (= 11+50),
-norm weights 12 and 13, residual seed M, sublayer output seed M+1.
+norm weights 12 and 13, residual seed M, sublayer output seed M+1. The head mix (fn [4, 4H],
+base [4], scale [1]; the test page draws none) uses the same distributions with seed 71.
 """
 from __future__ import annotations
 
@@ -32,6 +33,7 @@ SEED_ATTN = 11
 SEED_FFN = 61
 SEED_NORM_ATTN = 12
 SEED_NORM_FFN = 13
+SEED_HEAD = 71
 
 
 def hc_params(seed: int, H: int = H, hc: int = HC):
@@ -41,6 +43,16 @@ def hc_params(seed: int, H: int = H, hc: int = HC):
     fn = torch.randn(mix, hc * H, generator=g) * 0.0225
     base = torch.randn(mix, generator=g) * 3
     scale = torch.rand(3, generator=g) * 0.05 + 0.01
+    return fn.contiguous(), scale.contiguous(), base.contiguous()
+
+
+def hc_head_params(seed: int, H: int = H, hc: int = HC):
+    """(fn fp32 [hc, hc*H], scale fp32 [1], base fp32 [hc]) for the head mix, with the
+    distributions of the site parameters, drawn in the order fn, base, scale."""
+    g = torch.Generator().manual_seed(seed)
+    fn = torch.randn(hc, hc * H, generator=g) * 0.0225
+    base = torch.randn(hc, generator=g) * 3
+    scale = torch.rand(1, generator=g) * 0.05 + 0.01
     return fn.contiguous(), scale.contiguous(), base.contiguous()
 
 

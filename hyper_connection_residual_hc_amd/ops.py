@@ -454,3 +454,36 @@ def mxfp8_swizzle_128x4(scales: torch.Tensor, out: Optional[torch.Tensor] = None
     _lib.call("mxfp8_swizzle_128x4", scales.data_ptr(), _rows(scales, G), M, G, out.data_ptr(),
               _stream(scales))
     return out
+
+
+# ---- hc_head ----------------------------------------------------------------------------------
+def head_fn_pack(fn: torch.Tensor) -> torch.Tensor:
+    """fp32 head fn [4, 4H] -> the packed operands hc_head reads."""
+    _need(fn, "fn", torch.float32, 2)
+    if fn.shape[0] != HC or fn.shape[1] % HC or not fn.is_contiguous():
+        raise ValueError(f"fn must be a contiguous [{HC}, 4H] tensor, got {tuple(fn.shape)}")
+    H = fn.shape[1] // HC
+    nbytes = fn_packed_bytes(H)
+    if nbytes == 0:
+        raise ValueError(f"unsupported H={H}")
+    out = torch.empty(nbytes // 2, dtype=torch.int16, device=fn.device)
+    _lib.call("hc_head_fn_pack", fn.data_ptr(), H, out.data_ptr(), _stream(fn))
+    return out
+
+
+def head(R: torch.Tensor, fn_packed: torch.Tensor, scale: torch.Tensor, base: torch.Tensor,
+         norm_eps: float = RMS_EPS, hc_eps: float = HC_EPS, out: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y bf16 [M, H] = sum_i pre_i R_i with pre = sigmoid(mixes * scale + base) + hc_eps."""
+    M, H, ldR = _residual(R)
+    _packed(fn_packed, H)
+    _contig(scale, "scale", torch.float32, (1,))
+    _contig(base, "base", torch.float32, (HC,))
+    if out is None:
+        out = torch.empty(M, H, dtype=torch.bfloat16, device=R.device)
+    _shaped(out, "out", torch.bfloat16, (M, H))
+    ws = _workspace(int(_lib.lib().hc_head_workspace_bytes(M, H)), R.device, workspace)
+    _lib.call("hc_head", R.data_ptr(), ldR, fn_packed.data_ptr(), scale.data_ptr(),
+              base.data_ptr(), M, H, norm_eps, hc_eps, out.data_ptr(), _rows(out, H),
+              ws.data_ptr(), ws.numel() * ws.element_size(), _stream(R))
+    return out

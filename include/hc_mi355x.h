@@ -270,6 +270,27 @@ HC_API size_t mxfp8_swizzled_bytes(int64_t M, int32_t G);
 HC_API int mxfp8_swizzle_128x4(const uint8_t* scales, int64_t ldS, int64_t M, int32_t G,
                                uint8_t* out, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * hc_head: the model's last mix of the 4 streams into one (deepseek_v4.py, hc_head_torch and
+ * the model's hc_head / fused_hc_head; make_hc_head_params: fn fp32 [4, 4H], base [4],
+ * scale [1]). Per row, with x = R[m] flattened stream-major (4H values):
+ *   mixes[i] = (sum_k fn[i, k] x_k) * rsqrt(sum x^2 / 4H + norm_eps)        i = 0..3
+ *   pre[i]   = sigmoid(mixes[i] * scale[0] + base[i]) + hc_eps
+ *   y[m, h]  = bf16_rne( sum_i pre[i] * R[m, i, h] )        (no norm: the model's final
+ *                                                            RMSNorm is a separate step)
+ * hc_head_fn_pack packs the 4-row fn into the layout of hc_fn_pack (hc_fn_packed_bytes(H)
+ * bytes; the other rows are zero), once per weight.
+ *
+ * R: bf16 [M, 4, H] (ldR); scale fp32 [1]; base fp32 [4]; y: bf16 [M, H] (ldY), written.
+ * H: as hc_pre. workspace: >= hc_head_workspace_bytes(M, H), 256-byte aligned.
+ * ------------------------------------------------------------------------------------- */
+HC_API int hc_head_fn_pack(const float* fn, int32_t H, uint16_t* fn_packed, void* stream);
+HC_API size_t hc_head_workspace_bytes(int64_t M, int32_t H);
+HC_API int hc_head(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, const float* scale,
+                   const float* base, int64_t M, int32_t H, float norm_eps, float hc_eps,
+                   uint16_t* y, int64_t ldY, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif
