@@ -138,7 +138,7 @@ struct PipeArgs {
 struct LdsLayout {
   uint16_t ring[2][kSlotElems];                  // 64 KB
   float epi[2][kHC][kStatsRows][kEpiCols];       // 66 KB
-  float coef[2][kStatsRows][kCoefs];             // 10 KB
+  float coef[4][kStatsRows][kCoefs];             // 20 KB: two tile pairs
 };
 
 __device__ __forceinline__ int swz(int row, int unit) { return unit ^ (row & 15); }
@@ -158,7 +158,22 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
   const int hs = s * (H / kSlices);
   if (total == 0) return;  // block-uniform: no barrier is skipped by part of the block
 
-  auto tile_of = [&](int sigma) { return kb + (sigma / nstage) * a.blocks_per_slice; };
+  // Stage schedule. The block's tiles go in pairs (tile iterations 2k, 2k+1) whose stages
+  // interleave, (2k, p), (2k+1, p), (2k, p+1), ...: consecutive stages cover the same columns,
+  // so the consumers load each stage's fn operands once for two tiles. An odd last tile runs
+  // its stages alone. nstage = H / 512 is even, so a paired part is a multiple of four stages.
+  const int npair = my_tiles >> 1;
+  const int paired = npair * 2 * nstage;
+  auto sched = [&](int sigma, int& ti, int& p) __attribute__((always_inline)) {
+    if (sigma < paired) {
+      const int k = sigma / (2 * nstage), j = sigma - k * 2 * nstage;
+      p = j >> 1;
+      ti = 2 * k + (j & 1);
+    } else {
+      p = sigma - paired;
+      ti = 2 * npair;
+    }
+  };
 
   if (wave < 4) {
     // ===================================== producers ======================================
@@ -171,10 +186,12 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
     // this block's packed fn slice, which the consumers keep in the L2, not HBM. (A slice
     // holds 40H elements; the loads span 3H + 512.)
     const uint16_t* dead = a.fnp + (int64_t)s * chunks_per_slice(H) * kPackTiles * 64 * 8 + lane * 8;
-    auto issue = [&](int sigma, u32x4 (&d)[kItemsPerLane][kHC + 1]) {
+    auto issue = [&](int sigma, u32x4 (&d)[kItemsPerLane][kHC + 1]) __attribute__((always_inline)) {
       const bool live = sigma < total;  // block-uniform
       const int sg = min(sigma, total - 1);
-      const int T = tile_of(sg), p = sg - (sg / nstage) * nstage;
+      int ti, p;
+      sched(sg, ti, p);
+      const int T = kb + ti * a.blocks_per_slice;
       const int h = hs + 64 * p + 8 * hg;
 #pragma unroll
       for (int it = 0; it < kItemsPerLane; ++it) {
@@ -185,8 +202,10 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
         if (kPost) d[it][kHC] = ld16_stream(live ? a.x + (int64_t)row * a.ldX + h : dead);
       }
     };
-    auto produce = [&](int sigma, u32x4 (&d)[kItemsPerLane][kHC + 1]) {
-      const int T = tile_of(sigma), p = sigma - (sigma / nstage) * nstage;
+    auto produce = [&](int sigma, u32x4 (&d)[kItemsPerLane][kHC + 1]) __attribute__((always_inline)) {
+      int ti, p;
+      sched(sigma, ti, p);
+      const int T = kb + ti * a.blocks_per_slice;
       uint16_t* slot = L.ring[sigma & 1];
 #pragma unroll
       for (int it = 0; it < kItemsPerLane; ++it) {
@@ -194,7 +213,7 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
         u32x4 st[kHC];
         if (kPost) {
           const int row = min(T * kStatsRows + lrow, M - 1);
-          const float* cf = L.coef[(sigma / nstage) & 1][lrow];
+          const float* cf = L.coef[ti & 3][lrow];
           float pj[kHC], cij[kHC][kHC];
 #pragma unroll
           for (int j = 0; j < kHC; ++j) pj[j] = cf[j];
@@ -242,7 +261,7 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
     // were issued four stages earlier. The trip has no branch: every path from one stage to
     // the next issues the same memory operations, so the compiler's in-order wait counts stay
     // exact and each stage waits only for its own loads, not for the three stages behind it.
-    auto trip = [&](int sg) {
+    auto trip = [&](int sg) __attribute__((always_inline)) {
       produce(sg, ld0);
       issue(sg + 4, ld0);
       __syncthreads();
@@ -284,19 +303,18 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
     const int q = wave - 4;  // stream
     const int r16 = lane & 15, g = lane >> 4;
     const u32x4* bslice = reinterpret_cast<const u32x4*>(a.fnp) + (int64_t)s * chunks_per_slice(H) * kPackTiles * 64 + lane;
-    f32x4 d0[4], d1[4], sq[4];
-    auto zero_acc = [&]() {
+    // accumulators of the even (A) and odd (B) tile of a pair
+    f32x4 aD0[4], aD1[4], aSq[4], bD0[4], bD1[4], bSq[4];
+    auto zero = [&](f32x4 (&v)[4]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        d0[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-        d1[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sq[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int sub = 0; sub < 4; ++sub) v[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
-    // post / comb of tile T's 64 rows into coefficient slot T & 1 (fused form)
-    auto load_coef = [&](int tile_iter) {
-      const int T = kb + tile_iter * a.blocks_per_slice;
-      float* dst = &L.coef[tile_iter & 1][0][0];
+    zero(aD0), zero(aD1), zero(aSq), zero(bD0), zero(bD1), zero(bSq);
+    // post / comb of tile iteration ti's 64 rows into coefficient slot ti & 3 (fused form)
+    auto load_coef = [&](int ti) __attribute__((always_inline)) {
+      if (ti >= my_tiles) return;  // block-uniform
+      const int T = kb + ti * a.blocks_per_slice;
+      float* dst = &L.coef[ti & 3][0][0];
       for (int v = threadIdx.x - 256; v < kStatsRows * 5; v += 256) {
         const int lr = v / 5, k = v - lr * 5;
         const int row = min(T * kStatsRows + lr, M - 1);
@@ -304,10 +322,10 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
         *reinterpret_cast<f32x4*>(dst + lr * kCoefs + 4 * k) = *reinterpret_cast<const f32x4*>(src);
       }
     };
-    // partials of tile T from epilogue slot T & 1
-    auto flush = [&](int tile_iter) {
-      const int T = kb + tile_iter * a.blocks_per_slice;
-      const auto& ep = L.epi[tile_iter & 1];
+    // partials of tile iteration ti from epilogue slot ti & 1
+    auto flush = [&](int ti) __attribute__((always_inline)) {
+      const int T = kb + ti * a.blocks_per_slice;
+      const auto& ep = L.epi[ti & 1];
       for (int idx = threadIdx.x - 256; idx < kStatsRows * (kMix + 1); idx += 256) {
         const int row = idx / (kMix + 1);
         const int f = idx - row * (kMix + 1);
@@ -327,75 +345,114 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
         a.part[((int64_t)s * M + grow) * kPartStride + f] = v;
       }
     };
+    int pending = -1;  // tile whose epilogue slot waits for its flush
 
-    // fn operands of stage k (clamped to the last stage, so the prefetch past the end reloads
-    // valid memory) for this consumer's two chunks
-    auto load_b = [&](int k, u32x4 (&b)[2][kPackTiles]) {
-      const int kk = min(k, total - 1);
-      const int p = kk - (kk / nstage) * nstage;
+    // fn operands of stage st (clamped to the last stage, so loads past the end read valid
+    // memory) for this consumer's two chunks
+    auto load_b = [&](int st, u32x4 (&b)[2][kPackTiles]) __attribute__((always_inline)) {
+      int ti, p;
+      sched(min(st, total - 1), ti, p);
 #pragma unroll
       for (int hq = 0; hq < 2; ++hq)
 #pragma unroll
         for (int t = 0; t < kPackTiles; ++t)
           b[hq][t] = bslice[((int64_t)(p * kStageChunks + 2 * q + hq) * kPackTiles + t) * 64];
     };
-    // iteration sigma: the next tile's coefficients (fused form), the previous tile's partials,
-    // the prefetch of stage sigma's fn operands, then stage sigma - 1's MFMAs
-    auto step = [&](int sigma, u32x4 (&bnext)[2][kPackTiles], const u32x4 (&bcur)[2][kPackTiles]) {
-      const int prev = sigma - 1;
-      if (kPost && sigma < total && (sigma + 1) % nstage == 0 && (sigma + 1) / nstage < my_tiles)
-        load_coef((sigma + 1) / nstage);  // used by the producers from sigma + 1
-      if (prev >= nstage && prev % nstage == 0) flush(prev / nstage - 1);
-      load_b(sigma, bnext);
-      if (prev >= 0) {
-        const int p = prev - (prev / nstage) * nstage;
-        const uint16_t* slot = L.ring[prev & 1];
+    // the MFMAs of stage st from its ring slot; at a tile's last stage the accumulators go to
+    // its epilogue slot (16x16 layout: lane holds rows 4*(lane/16) + i of column lane % 16)
+    auto mma = [&](int st, const u32x4 (&b)[2][kPackTiles], f32x4 (&d0)[4], f32x4 (&d1)[4],
+                   f32x4 (&sq)[4]) __attribute__((always_inline)) {
+      int ti, p;
+      sched(st, ti, p);
+      const uint16_t* slot = L.ring[st & 1];
 #pragma unroll
-        for (int hq = 0; hq < 2; ++hq) {
+      for (int hq = 0; hq < 2; ++hq) {
 #pragma unroll
-          for (int sub = 0; sub < 4; ++sub) {
-            const int row = 16 * sub + r16;
-            const u32x4 av = *reinterpret_cast<const u32x4*>(&slot[row * kRowElems + 8 * swz(row, 8 * q + 4 * hq + g)]);
-            const bf16x8 xa = __builtin_bit_cast(bf16x8, av);
-            d0[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, bcur[hq][0]), d0[sub], 0, 0, 0);
-            d1[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, bcur[hq][3]), d1[sub], 0, 0, 0);
-            sq[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, xa, sq[sub], 0, 0, 0);
-            d0[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, bcur[hq][1]), d0[sub], 0, 0, 0);
-            d1[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, bcur[hq][4]), d1[sub], 0, 0, 0);
-            d0[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, bcur[hq][2]), d0[sub], 0, 0, 0);
-          }
-        }
-        if (p == nstage - 1) {
-          // tile done: accumulators into its epilogue slot (16x16 layout: lane holds rows
-          // 4*(lane/16) + i of column lane % 16), flushed in the iteration after the barrier
-          auto& ep = L.epi[(prev / nstage) & 1][q];
-#pragma unroll
-          for (int sub = 0; sub < 4; ++sub) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int row = sub * 16 + 4 * g + i;
-              ep[row][r16] = d0[sub][i];
-              ep[row][16 + r16] = d1[sub][i];
-              if (r16 == 4 * g + i) ep[sub * 16 + r16][32] = sq[sub][i];
-            }
-          }
-          zero_acc();
+        for (int sub = 0; sub < 4; ++sub) {
+          const int row = 16 * sub + r16;
+          const u32x4 av = *reinterpret_cast<const u32x4*>(&slot[row * kRowElems + 8 * swz(row, 8 * q + 4 * hq + g)]);
+          const bf16x8 xa = __builtin_bit_cast(bf16x8, av);
+          d0[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[hq][0]), d0[sub], 0, 0, 0);
+          d1[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[hq][3]), d1[sub], 0, 0, 0);
+          sq[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, xa, sq[sub], 0, 0, 0);
+          d0[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[hq][1]), d0[sub], 0, 0, 0);
+          d1[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[hq][4]), d1[sub], 0, 0, 0);
+          d0[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[hq][2]), d0[sub], 0, 0, 0);
         }
       }
-      __syncthreads();
+      if (p == nstage - 1) {
+        auto& ep = L.epi[ti & 1][q];
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = sub * 16 + 4 * g + i;
+            ep[row][r16] = d0[sub][i];
+            ep[row][16 + r16] = d1[sub][i];
+            if (r16 == 4 * g + i) ep[sub * 16 + r16][32] = sq[sub][i];
+          }
+        }
+        zero(d0), zero(d1), zero(sq);
+        pending = ti;  // flushed in the next iteration, after the barrier
+      }
+    };
+    // start of iteration i: the coefficients of the tile pair after the one whose stages the
+    // producers start now (fused form), and the flush of a finished tile
+    auto begin = [&](int i) __attribute__((always_inline)) {
+      if (kPost && i < paired && i % (2 * nstage) == 0) {
+        const int k = i / (2 * nstage);
+        load_coef(2 * k + 2);
+        load_coef(2 * k + 3);
+      }
+      if (pending >= 0) {
+        flush(pending);
+        pending = -1;
+      }
     };
 
-    zero_acc();
-    if (kPost) load_coef(0);
-    __syncthreads();  // matches the producers' prologue barrier
-    // stage k's operands live in buffer k % 2; two iterations per trip keep fixed registers
-    u32x4 b0[2][kPackTiles], b1[2][kPackTiles];
-    for (int sigma = 0; sigma <= total; sigma += 2) {
-      step(sigma, b0, b1);
-      if (sigma + 1 > total) break;
-      step(sigma + 1, b1, b0);
+    if (kPost) {
+      load_coef(0);
+      load_coef(1);
     }
-    flush(my_tiles - 1);
+    __syncthreads();  // matches the producers' prologue barrier
+    // Iteration i multiplies stage i - 1 (written by the producers in iteration i - 1) and ends
+    // with the block barrier. Operands: a paired stage couple (2u, 2u + 1) shares the buffer
+    // of unit u (bX for even u, bY for odd u), loaded in iteration 2u; a lone stage st has its
+    // own, loaded in iteration st (bX for even st, bY for odd).
+    u32x4 bX[2][kPackTiles], bY[2][kPackTiles];
+    for (int i = 0; i < paired; i += 4) {
+      begin(i);
+      load_b(i, bX);
+      if (i > 0) mma(i - 1, bY, bD0, bD1, bSq);
+      __syncthreads();
+      begin(i + 1);
+      mma(i, bX, aD0, aD1, aSq);
+      __syncthreads();
+      begin(i + 2);
+      load_b(i + 2, bY);
+      mma(i + 1, bX, bD0, bD1, bSq);
+      __syncthreads();
+      begin(i + 3);
+      mma(i + 2, bY, aD0, aD1, aSq);
+      __syncthreads();
+    }
+    // iteration `paired`: the last paired stage and the operands of the first lone stage
+    begin(paired);
+    load_b(paired, bX);
+    if (paired > 0) mma(paired - 1, bY, bD0, bD1, bSq);
+    __syncthreads();
+    // the lone tile's stages (none when the tile count is even); total - paired is even
+    for (int i = paired + 1; i <= total; i += 2) {
+      begin(i);
+      load_b(i, bY);
+      mma(i - 1, bX, aD0, aD1, aSq);
+      __syncthreads();
+      begin(i + 1);
+      load_b(i + 1, bX);
+      mma(i, bY, aD0, aD1, aSq);
+      __syncthreads();
+    }
+    if (pending >= 0) flush(pending);
   }
 }
 
