@@ -170,29 +170,15 @@ __device__ __forceinline__ float mx_inv_scale(int e) {
   return __uint_as_float((uint32_t)(127 - e) << 23);
 }
 
-// fp32 -> e4m3fn code, round to nearest even, saturating to +-448 (0x7E / 0xFE), sign of zero
-// kept. Exponent bias 7, 3 mantissa bits; below 2^-6 the codes are multiples of 2^-9.
-__device__ __forceinline__ uint32_t e4m3_code(float s) {
-  const uint32_t u = __float_as_uint(s);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  uint32_t code;
-  if (a >= 0x3C800000u) {  // |s| >= 2^-6: normal e4m3 after rounding
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);  // round to 3 mantissa bits, ties even
-    const int ex = (int)(r >> 23) - 127 + 7;
-    const uint32_t man = (r >> 20) & 7u;
-    code = (ex > 15 || (ex == 15 && man == 7u)) ? 0x7Eu : (((uint32_t)ex << 3) | man);
-  } else {  // subnormal range: multiples of 2^-9, rounded to nearest even
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  }
-  return code | sign;
-}
-
-// Four bf16 values in two packed words, w0 = (v0, v1) and w1 = (v2, v3), scaled by inv
-// -> four e4m3 codes in one word, v0 in the low byte.
+// Four bf16 values in two packed words, w0 = (v0, v1) and w1 = (v2, v3), scaled by inv (a
+// power of two) -> four e4m3fn codes in one word, v0 in the low byte: the matrix-core-era
+// conversion v_cvt_pk_fp8_f32 (OCP e4m3fn on gfx950), round to nearest even, sign of zero
+// kept, subnormals down to 2^-9. Its overflow result is NaN rather than +-448, which the MX
+// scale rule never reaches: every scaled value is at most 448.
 __device__ __forceinline__ uint32_t e4m3_word(uint32_t w0, uint32_t w1, float inv) {
-  return e4m3_code(bf_lo(w0) * inv) | (e4m3_code(bf_hi(w0) * inv) << 8) |
-         (e4m3_code(bf_lo(w1) * inv) << 16) | (e4m3_code(bf_hi(w1) * inv) << 24);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(bf_lo(w0) * inv, bf_hi(w0) * inv, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(bf_lo(w1) * inv, bf_hi(w1) * inv, r, true);
+  return (uint32_t)r;
 }
 
 // Largest magnitude bits (low 15 bits) of 8 packed bf16.

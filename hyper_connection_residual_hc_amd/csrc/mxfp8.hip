@@ -5,49 +5,56 @@
 // smallest e with amax * 2^-e <= 448), scale byte e + 127; elements y * 2^-e (exact in fp32)
 // rounded to nearest even into e4m3fn, saturating at +-448, with the sign of zero kept.
 //
-// One thread per block: 64 bytes in (4 x 16-byte loads), 32 code bytes out (2 x 16-byte
-// stores) and one scale byte; consecutive lanes take consecutive blocks of a row.
+// One lane per 8 consecutive values (a 16-byte load, an 8-byte store of codes), eight such
+// units in flight per lane: a lane quad holds a 32-value block, whose maximum comes from a
+// quad DPP max; the quad's first lane writes the scale byte.
 #include "hc_launch.h"
 
 namespace hc {
 
+constexpr int kMxUnits = 8;  // 16-byte loads in flight per lane
+
 __global__ __launch_bounds__(256) void mxfp8_kernel(const uint16_t* __restrict__ y, int64_t ldY,
-                                                    int M, int G, uint8_t* __restrict__ q,
-                                                    int64_t ldQ, uint8_t* __restrict__ sc,
-                                                    int64_t ldS) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int m = (int)(gid / G);
-  if (m >= M) return;
-  const int g = (int)(gid - (int64_t)m * G);
-  const uint16_t* src = y + (int64_t)m * ldY + g * 32;
-  u32x4 v[4];
+                                                    int M, int U, int chunks,
+                                                    uint8_t* __restrict__ q, int64_t ldQ,
+                                                    uint8_t* __restrict__ sc, int64_t ldS) {
+  // A unit is 8 consecutive values of a row; U = K / 8 units per row, a multiple of 4. A wave
+  // takes 512 units of one row (chunk j): lane l holds units 512 j + 64 t + l, t < 8, so each
+  // load instruction reads 1 KB contiguous and the lane quads hold whole 32-value blocks.
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int m = (int)(wid / chunks);
+  if (m >= M) return;  // wave-uniform
+  const int j = (int)(wid - (int64_t)m * chunks);
+  const uint16_t* yr = y + (int64_t)m * ldY;
+  u32x4 v[kMxUnits];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = ld16_stream(src + 8 * i);
-
-  uint32_t amax = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) amax = max(amax, amax_bits8(v[i]));
-  const int e = mx_block_exponent(amax);
-  sc[(int64_t)m * ldS + g] = (uint8_t)(e + 127);
-  const float inv = mx_inv_scale(e);
-
-  u32x4 out[2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[i >> 1][(i & 1) * 2] = e4m3_word(v[i][0], v[i][1], inv);
-    out[i >> 1][(i & 1) * 2 + 1] = e4m3_word(v[i][2], v[i][3], inv);
+  for (int t = 0; t < kMxUnits; ++t) {
+    const int u = 512 * j + 64 * t + lane;
+    v[t] = ld16_stream(yr + 8 * (int64_t)min(u, U - 1));  // past the row's end: a valid unit
   }
-  uint8_t* dst = q + (int64_t)m * ldQ + g * 32;
-  st16_stream(dst, out[0]);
-  st16_stream(dst + 16, out[1]);
+#pragma unroll
+  for (int t = 0; t < kMxUnits; ++t) {
+    const int u = 512 * j + 64 * t + lane;  // quads past the end are whole quads (U % 4 == 0)
+    const int e = mx_block_exponent(quad_max_u32(amax_bits8(v[t])));
+    if (u < U) {
+      const float inv = mx_inv_scale(e);
+      u32x2 codes;
+      codes[0] = e4m3_word(v[t][0], v[t][1], inv);
+      codes[1] = e4m3_word(v[t][2], v[t][3], inv);
+      __builtin_nontemporal_store(codes, reinterpret_cast<u32x2*>(q + (int64_t)m * ldQ + 8 * (int64_t)u));
+      if ((u & 3) == 0) sc[(int64_t)m * ldS + (u >> 2)] = (uint8_t)(e + 127);
+    }
+  }
 }
 
 hipError_t launch_mxfp8(const uint16_t* y, int64_t ldY, int M, int K, uint8_t* q, int64_t ldQ,
                         uint8_t* scales, int64_t ldS, hipStream_t s) {
-  const int G = K / 32;
-  const int64_t threads = (int64_t)M * G;
-  hipLaunchKernelGGL(mxfp8_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, y,
-                     ldY, M, G, q, ldQ, scales, ldS);
+  const int U = K / 8;
+  const int chunks = (U + 64 * kMxUnits - 1) / (64 * kMxUnits);
+  const int64_t waves = (int64_t)M * chunks;
+  hipLaunchKernelGGL(mxfp8_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, y, ldY,
+                     M, U, chunks, q, ldQ, scales, ldS);
   return hipGetLastError();
 }
 
