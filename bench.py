@@ -110,6 +110,71 @@ def cpu_baseline(rows: int, target_s: float):
     return done / el, threads, el, done
 
 
+def ops_table(args, sets, fnp, sc, ba, w, torch, ops, inputs, d) -> int:
+    """Every entry point alone on the bench's rotating M=4096 input sets: one JSON line each
+    with the wall-clock time per call and the algorithmic bytes it moves."""
+    M = M_BENCH
+    dev = sets[0][0].device
+    fh, sh, bh = map(d, inputs.hc_head_params(inputs.SEED_HEAD))
+    fnp_h = ops.head_fn_pack(fh)
+    extra = []
+    for R, x, post, comb, o in sets:
+        mixes = torch.empty(M, 24, device=dev)
+        ops.pre_stats(R, fnp, mixes=mixes, want_sumsq=False, workspace=o["ws"])
+        pre = torch.empty(M, HC, device=dev)
+        y = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
+        ops.combine_norm(R, post, w, out=y)
+        extra.append(dict(mixes=mixes, pre=pre, y=y,
+                          q=torch.empty(M, H, dtype=torch.uint8, device=dev),
+                          s=torch.empty(M, H // 32, dtype=torch.uint8, device=dev),
+                          sw=torch.empty(M * H // 32, dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+    coef_o = 4 * (HC + HC + HC * HC)  # pre, post, comb written
+    table = {
+        "hc_post": (lambda k, s, e: ops.post(s[1], s[0], s[2], s[3], out=s[4]["R1"]),
+                    M * POST_BYTES_ROW),
+        "hc_pre_stats": (lambda k, s, e: ops.pre_stats(s[0], fnp, mixes=e["mixes"], want_sumsq=False,
+                                                       workspace=s[4]["ws"]),
+                         M * (2 * HC * H + 4 * 24) + FN_BYTES),
+        "hc_sinkhorn": (lambda k, s, e: ops.sinkhorn(e["mixes"], sc, ba,
+                                                     out=(e["pre"], s[4]["post"], s[4]["comb"])),
+                        M * (4 * 24 + coef_o)),
+        "hc_combine_norm": (lambda k, s, e: ops.combine_norm(s[0], s[2], w, out=s[4]["y"]),
+                            M * (2 * HC * H + 4 * HC + 2 * H) + 2 * H),
+        "hc_pre": (lambda k, s, e: ops.pre(s[0], fnp, sc, ba, w,
+                                           out=(s[4]["y"], s[4]["post"], s[4]["comb"], None),
+                                           workspace=s[4]["ws"]),
+                   M * PRE_BYTES_ROW + PRE_BYTES_CALL),
+        "hc_post_pre": (lambda k, s, e: ops.post_pre(s[1], s[0], s[2], s[3], fnp, sc, ba, w,
+                                                     out=(s[4]["R1"], s[4]["y"], s[4]["post"],
+                                                          s[4]["comb"], None),
+                                                     workspace=s[4]["ws"]),
+                        M * (POST_BYTES_ROW + 2 * H + 4 * (HC + HC * HC)) + PRE_BYTES_CALL),
+        "hc_pre_mxfp8 (no bf16 y)": (lambda k, s, e: ops.pre_mxfp8(
+            s[0], fnp, sc, ba, w, out=(None, e["q"], e["s"], s[4]["post"], s[4]["comb"], None),
+            workspace=s[4]["ws"]), M * (2 * HC * H + H + H // 32 + 4 * (HC + HC * HC)) + PRE_BYTES_CALL),
+        "mxfp8_quant_rows": (lambda k, s, e: ops.mxfp8_quant_rows(e["y"], q=e["q"], scales=e["s"]),
+                             M * (2 * H + H + H // 32)),
+        "mxfp8_swizzle_128x4": (lambda k, s, e: ops.mxfp8_swizzle_128x4(e["s"], out=e["sw"]),
+                                M * 2 * (H // 32)),
+        "hc_head": (lambda k, s, e: ops.head(s[0], fnp_h, sh, bh, out=e["y"], workspace=s[4]["ws"]),
+                    M * (2 * HC * H + 2 * H) + 4 * HC * 4 * H),
+    }
+    for name, (fn_, nbytes) in table.items():
+        for k in range(args.warmup):
+            fn_(k, sets[k % len(sets)], extra[k % len(sets)])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            fn_(k, sets[k % len(sets)], extra[k % len(sets)])
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / args.steps
+        print(json.dumps({"op": name, "M": M, "H": H, "us_per_call_wall": us,
+                          "algorithmic_bytes": nbytes,
+                          "algorithmic_gbps_wall": nbytes / (us * 1e-6) / 1e9}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +184,10 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ops", action="store_true",
+                    help="instead of the step: time every entry point alone at M=4096 and print "
+                         "one JSON line per entry point (wall clock per call; run it under "
+                         "rocprofv3 --kernel-trace for kernel durations)")
     ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
                     help="fused: hc_post_pre (post with the next pre's mix stats in one pass, "
                          "then the pre finish); unfused: hc_post then hc_pre")
@@ -156,6 +225,8 @@ def main() -> int:
                     ws=torch.empty(ops.pre_workspace_bytes(M, H), dtype=torch.uint8, device=dev))
         sets.append((R, x, post, comb, outs))
     torch.cuda.synchronize()
+    if args.ops:
+        return ops_table(args, sets, fnp_f, sc_f, ba_f, w_f, torch, ops, inputs, d)
 
     def step(k):
         """One step as the product runs it: no events inside."""
