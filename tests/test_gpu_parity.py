@@ -251,11 +251,12 @@ def ffn():
     return gu.Site(inputs.SEED_FFN, inputs.SEED_NORM_FFN)
 
 
-@pytest.mark.parametrize("M", [1, 63, 65, 300, 2112, 4096])
+@pytest.mark.parametrize("M", [1, 63, 65, 300, 2112, 4096, 6144])
 def test_fused_post_pre_equals_post_then_pre(attn, ffn, M):
     """hc_post_pre gives the bits of hc_post followed by hc_pre on its output. M covers one
     partial tile, tile edges, fewer tiles than blocks, and more tiles than blocks (2112 rows =
-    33 tiles: one block per slice takes two tiles, the others one)."""
+    33 tiles: one block per slice takes a tile pair, the others a lone tile; 6144 rows = 96
+    tiles: three per block on 256 CUs, a pair then a lone tile)."""
     gu.say(f"hc_post_pre fused M={M}")
     R = gu.dev(inputs.residual(M, M + 5))
     x = gu.dev(inputs.sublayer_out(M, M + 6))
@@ -333,3 +334,70 @@ def test_binding_rejects_short_outputs(attn, ffn):
         ops.combine_norm(R, post, attn.w_d, out=short_y)
     with pytest.raises(ValueError):
         ops.pre_stats(R, attn.fnp[:-8])
+
+
+@pytest.mark.parametrize("Hs", [2048, 7168, 8192])
+def test_wider_hidden_sizes(Hs):
+    """The other compiled widths (4, 14 and 16 column blocks of 512 per lane; 4, 14 and 16
+    stages per slice): pre and post vs the oracle, the fused op vs post then pre."""
+    gu.say(f"H={Hs}")
+    site = gu.Site(15, 16, H_=Hs)
+    nxt = gu.Site(17, 18, H_=Hs)
+    M = 130
+    R = inputs.residual(M, 19, H=Hs)
+    y, post, comb, pre = ops.pre(gu.dev(R), site.fnp, site.scale_d, site.base_d, site.w_d,
+                                 want_pre=True)
+    ref = site.oracle_pre(inputs.bits(R))
+    gu.assert_mixes_close(gu.f32_np(ops.pre_stats(gu.dev(R), site.fnp)[0]), ref["mixes"])
+    gu.assert_coef_close(gu.f32_np(comb), ref["comb"], "comb")
+    gu.assert_bf16_close(gu.bits_of(y), ref["y"], "y")
+    x = gu.dev(inputs.sublayer_out(M, 20, H=Hs))
+    Rd = gu.dev(R)
+    full = ops.post_pre(x, Rd, post, comb, nxt.fnp, nxt.scale_d, nxt.base_d, nxt.w_d)
+    Rn = ops.post(x, Rd, post, comb)
+    y2, post2, comb2, _ = ops.pre(Rn, nxt.fnp, nxt.scale_d, nxt.base_d, nxt.w_d)
+    assert torch.equal(full[0].view(torch.int16), Rn.view(torch.int16))
+    assert torch.equal(full[1].view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(full[2], post2) and torch.equal(full[3], comb2)
+
+
+def test_graph_capture_replays_match_eager(attn, ffn):
+    """The fused step captured in a HIP graph (the entry points allocate nothing and clear no
+    memory, so they capture as plain kernel nodes): three replays, with unrelated eager work
+    and a synchronisation between them, each give the eager result."""
+    M = 1024
+    R = gu.dev(inputs.residual(M, 31))
+    x = gu.dev(inputs.sublayer_out(M, 32))
+    _, post, comb, _ = ops.pre(R, attn.fnp, attn.scale_d, attn.base_d, attn.w_d)
+    outs = (torch.empty_like(R), torch.empty(M, gu.H, dtype=torch.bfloat16, device=gu.DEV),
+            torch.empty(M, 4, device=gu.DEV), torch.empty(M, 4, 4, device=gu.DEV), None)
+    ws = torch.empty(ops.post_pre_workspace_bytes(M, gu.H), dtype=torch.uint8, device=gu.DEV)
+
+    def step():
+        ops.post_pre(x, R, post, comb, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d, out=outs,
+                     workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs[:4]]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = gu.dev(inputs.residual(M, 33))
+    for rep in range(3):
+        for t in outs[:4]:
+            t.view(torch.uint8).fill_(0xA5)
+        ops.post(x, other, post, comb)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(outs[:4], ref)):
+            if a.dtype == torch.bfloat16:
+                a, b = a.view(torch.int16), b.view(torch.int16)
+            assert torch.equal(a, b), (rep, k)
