@@ -303,7 +303,7 @@ def main() -> int:
     rows_s = M / (ms_step * 1e-3)
     step_gbs = STEP_BYTES / (ms_step * 1e-3) / 1e9
     result = {
-        "metric": "mHC pre+post rows/s at M=4096, H=5120 (1 MI355X)",
+        "metric": "mHC pre+post rows/s and achieved HBM GB/s at M=4096, H=5120 (1 MI355X)",
         "value": rows_s,
         "unit": "rows/s",
         "n_gpus": 1,

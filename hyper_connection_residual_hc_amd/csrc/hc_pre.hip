@@ -83,7 +83,9 @@ __device__ __forceinline__ void load_row(const uint16_t* __restrict__ Rr,
 
 // y's row: written as bf16 when yr is given, and with kMx also as MXFP8 (qr: e4m3 codes,
 // sr: one scale byte per 32 columns) quantised from the same bf16 values, with the rule of
-// mxfp8_quant_rows. A 32-column block is the 8 columns of each lane of a lane quad.
+// mxfp8_quant_rows. A 32-column block is the 8 columns of each lane of a lane quad. The row
+// is stored non-temporally: its consumer is another kernel, and dirty lines left in the L2
+// would only lengthen this kernel's end-of-kernel write-back.
 template <int NG, bool kMx>
 __device__ __forceinline__ void combine_norm_row(const RowTile<NG>& t, const float (&p)[kHC],
                                                  const uint16_t* __restrict__ w, float eps,
@@ -118,14 +120,14 @@ __device__ __forceinline__ void combine_norm_row(const RowTile<NG>& t, const flo
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (c[g][e] * rn) * wf[e];
     const u32x4 yb = pack8(o);
-    if (!kMx || yr) st16(yr + g * 512 + lane * 8, yb);
+    if (!kMx || yr) st16_stream(yr + g * 512 + lane * 8, yb);
     if constexpr (kMx) {
       const int ex = mx_block_exponent(quad_max_u32(amax_bits8(yb)));
       const float inv = mx_inv_scale(ex);
       u32x2 codes;
       codes[0] = e4m3_word(yb[0], yb[1], inv);
       codes[1] = e4m3_word(yb[2], yb[3], inv);
-      *reinterpret_cast<u32x2*>(qr + g * 512 + lane * 8) = codes;
+      __builtin_nontemporal_store(codes, reinterpret_cast<u32x2*>(qr + g * 512 + lane * 8));
       if ((lane & 3) == 0) sr[g * 16 + (lane >> 2)] = (uint8_t)(ex + 127);
     }
   }
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(256) void head_finish_kernel(
       for (int i = 1; i < kHC; ++i) a = __fmaf_rn(p[i], r[i][e], a);
       o[e] = a;
     }
-    st16(yr + g * 512 + lane * 8, pack8(o));
+    st16_stream(yr + g * 512 + lane * 8, pack8(o));
   }
   (void)H;
 }
