@@ -91,6 +91,7 @@ def fn_pack(fn: torch.Tensor) -> torch.Tensor:
     if nbytes == 0:
         raise ValueError(f"unsupported H={H}")
     out = torch.empty(nbytes // 2, dtype=torch.int16, device=fn.device)
+    _one_device(fn, out)
     _lib.call("hc_fn_pack", fn.data_ptr(), H, out.data_ptr(), _stream(fn))
     return out
 
@@ -103,7 +104,17 @@ def stats_workspace_bytes(M: int, H: int) -> int:
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
     if workspace is None:
         return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
     return workspace
+
+
+def _one_device(*ts) -> None:
+    """Every tensor argument of a call on the same ROCm device (the kernels run on that
+    device's stream and read every pointer there)."""
+    devs = {t.device for t in ts if isinstance(t, torch.Tensor)}
+    if len(devs) != 1 or next(iter(devs)).type != "cuda":
+        raise ValueError(f"all tensors of a call must be on one ROCm device, got {sorted(map(str, devs))}")
 
 
 def pre_stats(R: torch.Tensor, fn_packed: torch.Tensor, rms_eps: float = RMS_EPS,
@@ -120,6 +131,7 @@ def pre_stats(R: torch.Tensor, fn_packed: torch.Tensor, rms_eps: float = RMS_EPS
     if sumsq is not None:
         _contig(sumsq, "sumsq", torch.float32, (M,))
     ws = _workspace(stats_workspace_bytes(M, H), R.device, workspace)
+    _one_device(R, fn_packed, mixes, sumsq, ws)
     _lib.call("hc_pre_stats", R.data_ptr(), ldR, fn_packed.data_ptr(), M, H, rms_eps,
               mixes.data_ptr(), _ptr(sumsq), ws.data_ptr(), ws.numel() * ws.element_size(),
               _stream(R))
@@ -143,6 +155,7 @@ def sinkhorn(mixes: torch.Tensor, scale: torch.Tensor, base: torch.Tensor, iters
     _contig(pre, "pre", torch.float32, (M, HC))
     _contig(post, "post", torch.float32, (M, HC))
     _contig(comb, "comb", torch.float32, (M, HC, HC))
+    _one_device(mixes, scale, base, pre, post, comb)
     _lib.call("hc_sinkhorn", mixes.data_ptr(), M, scale.data_ptr(), base.data_ptr(), iters,
               pre_eps, sinkhorn_eps, post_mult, pre.data_ptr(), post.data_ptr(), comb.data_ptr(),
               _stream(mixes))
@@ -161,6 +174,7 @@ def combine_norm(R: torch.Tensor, pre: torch.Tensor, weight: torch.Tensor,
     if out is None:
         out = torch.empty(M, H, dtype=torch.bfloat16, device=R.device)
     _shaped(out, "out", torch.bfloat16, (M, H))
+    _one_device(R, pre, weight, out)
     _lib.call("hc_combine_norm", R.data_ptr(), ldR, pre.data_ptr(), _rows(pre, HC),
               weight.data_ptr(), M, H, eps, out.data_ptr(), _rows(out, H), _stream(R))
     return out
@@ -180,6 +194,7 @@ def post(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.Tens
         out = torch.empty(M, HC, H, dtype=torch.bfloat16, device=R.device)
     _shaped(out, "out", torch.bfloat16, (M, HC, H))
     _residual(out)
+    _one_device(x, R, post_, comb, out)
     _lib.call("hc_post", x.data_ptr(), _rows(x, H), R.data_ptr(), ldR, post_.data_ptr(),
               comb.data_ptr(), M, H, out.data_ptr(), _rows(out, HC * H), _stream(R))
     return out
@@ -197,6 +212,7 @@ def mxfp8_quant_rows(y: torch.Tensor, q: Optional[torch.Tensor] = None,
         scales = torch.empty(M, K // 32, dtype=torch.uint8, device=y.device)
     _shaped(q, "q", torch.uint8, (M, K))
     _shaped(scales, "scales", torch.uint8, (M, K // 32))
+    _one_device(y, q, scales)
     _lib.call("mxfp8_quant_rows", y.data_ptr(), _rows(y, K), M, K, q.data_ptr(), _rows(q, K),
               scales.data_ptr(), _rows(scales, K // 32), _stream(y))
     return q, scales
@@ -231,6 +247,7 @@ def pre(R: torch.Tensor, fn_packed: torch.Tensor, scale: torch.Tensor, base: tor
     if pre_ is not None:
         _contig(pre_, "pre", torch.float32, (M, HC))
     ws = _workspace(pre_workspace_bytes(M, H), dev, workspace)
+    _one_device(R, fn_packed, scale, base, weight, y, post_, comb, pre_, ws)
     _lib.call("hc_pre", R.data_ptr(), ldR, fn_packed.data_ptr(), scale.data_ptr(),
               base.data_ptr(), weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters,
               post_mult, norm_eps, y.data_ptr(), _rows(y, H), _ptr(pre_), post_.data_ptr(),
@@ -277,6 +294,7 @@ def post_pre(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.
     if pre_o is not None:
         _contig(pre_o, "pre_out", torch.float32, (M, HC))
     ws = _workspace(post_pre_workspace_bytes(M, H), dev, workspace)
+    _one_device(x, R, post_, comb, fn_packed, scale, base, weight, Rn, y, post_o, comb_o, pre_o, ws)
     _lib.call("hc_post_pre", x.data_ptr(), _rows(x, H), R.data_ptr(), ldR, post_.data_ptr(),
               comb.data_ptr(), fn_packed.data_ptr(), scale.data_ptr(), base.data_ptr(),
               weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult,
@@ -304,6 +322,7 @@ def post_stats(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torc
     _shaped(out, "out", torch.bfloat16, (M, HC, H))
     _, _, ldOut = _residual(out)
     ws = _workspace(post_pre_workspace_bytes(M, H), R.device, workspace)
+    _one_device(x, R, post_, comb, fn_packed, out, ws)
     _lib.call("hc_post_stats", x.data_ptr(), _rows(x, H), R.data_ptr(), ldR, post_.data_ptr(),
               comb.data_ptr(), fn_packed.data_ptr(), M, H, out.data_ptr(), ldOut, ws.data_ptr(),
               ws.numel() * ws.element_size(), _stream(R))
@@ -333,6 +352,7 @@ def pre_finish(R: torch.Tensor, workspace: torch.Tensor, scale: torch.Tensor,
     _contig(comb_o, "comb", torch.float32, (M, HC, HC))
     if pre_o is not None:
         _contig(pre_o, "pre", torch.float32, (M, HC))
+    _one_device(R, workspace, scale, base, weight, y, post_o, comb_o, pre_o)
     _lib.call("hc_pre_finish", R.data_ptr(), ldR, scale.data_ptr(), base.data_ptr(),
               weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult,
               norm_eps, y.data_ptr(), _rows(y, H), _ptr(pre_o), post_o.data_ptr(),
@@ -383,6 +403,7 @@ def pre_mxfp8(R: torch.Tensor, fn_packed: torch.Tensor, scale: torch.Tensor, bas
     _contig(weight, "weight", torch.bfloat16, (H,))
     out = _mx_outputs(M, H, R.device, want_y, want_pre, out)
     ws = _workspace(pre_workspace_bytes(M, H), R.device, workspace)
+    _one_device(R, fn_packed, scale, base, weight, ws, *[t for t in out if t is not None])
     _lib.call("hc_pre_mxfp8", R.data_ptr(), ldR, fn_packed.data_ptr(), scale.data_ptr(),
               base.data_ptr(), weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters,
               post_mult, norm_eps, *_mx_args(out, H), ws.data_ptr(),
@@ -414,6 +435,7 @@ def post_pre_mxfp8(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: 
     _, _, ldOut = _residual(R_out)
     out = _mx_outputs(M, H, R.device, want_y, want_pre, out)
     ws = _workspace(post_pre_workspace_bytes(M, H), R.device, workspace)
+    _one_device(x, R, post_, comb, fn_packed, scale, base, weight, R_out, ws, *[t for t in out if t is not None])
     _lib.call("hc_post_pre_mxfp8", x.data_ptr(), _rows(x, H), R.data_ptr(), ldR,
               post_.data_ptr(), comb.data_ptr(), fn_packed.data_ptr(), scale.data_ptr(),
               base.data_ptr(), weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters,
@@ -433,6 +455,7 @@ def pre_finish_mxfp8(R: torch.Tensor, workspace: torch.Tensor, scale: torch.Tens
     _contig(base, "base", torch.float32, (MIX,))
     _contig(weight, "weight", torch.bfloat16, (H,))
     out = _mx_outputs(M, H, R.device, want_y, want_pre, out)
+    _one_device(R, workspace, scale, base, weight, *[t for t in out if t is not None])
     _lib.call("hc_pre_finish_mxfp8", R.data_ptr(), ldR, scale.data_ptr(), base.data_ptr(),
               weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult,
               norm_eps, *_mx_args(out, H), workspace.data_ptr(),
@@ -451,6 +474,7 @@ def mxfp8_swizzle_128x4(scales: torch.Tensor, out: Optional[torch.Tensor] = None
     _shaped(out, "out", torch.uint8, (nbytes,))
     if not out.is_contiguous():
         raise ValueError("out must be contiguous")
+    _one_device(scales, out)
     _lib.call("mxfp8_swizzle_128x4", scales.data_ptr(), _rows(scales, G), M, G, out.data_ptr(),
               _stream(scales))
     return out
@@ -467,6 +491,7 @@ def head_fn_pack(fn: torch.Tensor) -> torch.Tensor:
     if nbytes == 0:
         raise ValueError(f"unsupported H={H}")
     out = torch.empty(nbytes // 2, dtype=torch.int16, device=fn.device)
+    _one_device(fn, out)
     _lib.call("hc_head_fn_pack", fn.data_ptr(), H, out.data_ptr(), _stream(fn))
     return out
 
@@ -483,6 +508,7 @@ def head(R: torch.Tensor, fn_packed: torch.Tensor, scale: torch.Tensor, base: to
         out = torch.empty(M, H, dtype=torch.bfloat16, device=R.device)
     _shaped(out, "out", torch.bfloat16, (M, H))
     ws = _workspace(int(_lib.lib().hc_head_workspace_bytes(M, H)), R.device, workspace)
+    _one_device(R, fn_packed, scale, base, out, ws)
     _lib.call("hc_head", R.data_ptr(), ldR, fn_packed.data_ptr(), scale.data_ptr(),
               base.data_ptr(), M, H, norm_eps, hc_eps, out.data_ptr(), _rows(out, H),
               ws.data_ptr(), ws.numel() * ws.element_size(), _stream(R))

@@ -334,6 +334,11 @@ def test_binding_rejects_short_outputs(attn, ffn):
         ops.combine_norm(R, post, attn.w_d, out=short_y)
     with pytest.raises(ValueError):
         ops.pre_stats(R, attn.fnp[:-8])
+    with pytest.raises(ValueError):  # a host workspace would be a bad device pointer
+        ops.pre(R, attn.fnp, attn.scale_d, attn.base_d, attn.w_d,
+                workspace=torch.empty(ops.pre_workspace_bytes(M, gu.H), dtype=torch.uint8))
+    with pytest.raises(ValueError):  # so would a host weight
+        ops.combine_norm(R, post, attn.w_d.cpu())
 
 
 @pytest.mark.parametrize("Hs", [2048, 7168, 8192])
