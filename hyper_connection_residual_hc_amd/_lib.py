@@ -82,7 +82,7 @@ def lib() -> ctypes.CDLL:
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
-                f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                f"{LIB_PATH} is not built; run `python -m hyper_connection_residual_hc_amd.build` "
                 "(the mHC path has no implementation other than the HIP library)")
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
