@@ -416,40 +416,43 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
     }
     __syncthreads();  // matches the producers' prologue barrier
     // Iteration i multiplies stage i - 1 (written by the producers in iteration i - 1) and ends
-    // with the block barrier. Operands: a paired stage couple (2u, 2u + 1) shares the buffer
-    // of unit u (bX for even u, bY for odd u), loaded in iteration 2u; a lone stage st has its
-    // own, loaded in iteration st (bX for even st, bY for odd).
+    // with the block barrier. Operands: a paired stage couple (2u, 2u + 1) shares the buffer of
+    // unit u (bX for even u, bY for odd u); a lone stage st has its own (bX for even st, bY for
+    // odd). Each buffer is refilled right after the multiplications that last read it, so
+    // its operands are in flight for two iterations: the loads hit the L2 but return behind
+    // the HBM loads the producers issued before them.
     u32x4 bX[2][kPackTiles], bY[2][kPackTiles];
+    load_b(0, bX);
     for (int i = 0; i < paired; i += 4) {
       begin(i);
-      load_b(i, bX);
       if (i > 0) mma(i - 1, bY, bD0, bD1, bSq);
+      load_b(i + 2, bY);
       __syncthreads();
       begin(i + 1);
       mma(i, bX, aD0, aD1, aSq);
       __syncthreads();
       begin(i + 2);
-      load_b(i + 2, bY);
       mma(i + 1, bX, bD0, bD1, bSq);
+      load_b(i + 4, bX);  // past the paired part: the first lone stage
       __syncthreads();
       begin(i + 3);
       mma(i + 2, bY, aD0, aD1, aSq);
       __syncthreads();
     }
-    // iteration `paired`: the last paired stage and the operands of the first lone stage
+    // iteration `paired`: the last paired stage; the first lone stage's operands are in bX
     begin(paired);
-    load_b(paired, bX);
     if (paired > 0) mma(paired - 1, bY, bD0, bD1, bSq);
+    load_b(paired + 1, bY);
     __syncthreads();
     // the lone tile's stages (none when the tile count is even); total - paired is even
     for (int i = paired + 1; i <= total; i += 2) {
       begin(i);
-      load_b(i, bY);
       mma(i - 1, bX, aD0, aD1, aSq);
+      load_b(i + 1, bX);
       __syncthreads();
       begin(i + 1);
-      load_b(i + 1, bX);
       mma(i, bY, aD0, aD1, aSq);
+      load_b(i + 2, bY);
       __syncthreads();
     }
     if (pending >= 0) flush(pending);
