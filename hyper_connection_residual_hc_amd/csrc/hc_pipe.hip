@@ -138,7 +138,7 @@ struct PipeArgs {
 struct LdsLayout {
   uint16_t ring[2][kSlotElems];                  // 64 KB
   float epi[2][kHC][kStatsRows][kEpiCols];       // 66 KB
-  float coef[4][kStatsRows][kCoefs];             // 20 KB: two tile pairs
+  float coef[2][kStatsRows][kCoefs];             // 10 KB: two tiles
 };
 
 __device__ __forceinline__ int swz(int row, int unit) { return unit ^ (row & 15); }
@@ -158,11 +158,15 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
   const int hs = s * (H / kSlices);
   if (total == 0) return;  // block-uniform: no barrier is skipped by part of the block
 
-  // Stage schedule. The block's tiles go in pairs (tile iterations 2k, 2k+1) whose stages
-  // interleave, (2k, p), (2k+1, p), (2k, p+1), ...: consecutive stages cover the same columns,
-  // so the consumers load each stage's fn operands once for two tiles. An odd last tile runs
-  // its stages alone. nstage = H / 512 is even, so a paired part is a multiple of four stages.
-  const int npair = my_tiles >> 1;
+  // Stage schedule. Stats alone: the block's tiles go in pairs (tile iterations 2k, 2k+1)
+  // whose stages interleave, (2k, p), (2k+1, p), (2k, p+1), ...: consecutive stages cover the
+  // same columns, so the consumers load each stage's fn operands once for two tiles; an odd
+  // last tile runs its stages alone. nstage = H / 512 is even, so a paired part is a multiple
+  // of four stages. Fused form: the tiles run one after another. It moves five arrays in and
+  // four out, and HBM serves that mix faster when the rows in flight at once form a narrower
+  // band (64 rows per block instead of 128), which outweighs the doubled fn operand loads.
+  constexpr bool kPaired = !kPost;
+  const int npair = kPaired ? my_tiles >> 1 : 0;
   const int paired = npair * 2 * nstage;
   auto sched = [&](int sigma, int& ti, int& p) __attribute__((always_inline)) {
     if (sigma < paired) {
@@ -170,8 +174,9 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
       p = j >> 1;
       ti = 2 * k + (j & 1);
     } else {
-      p = sigma - paired;
-      ti = 2 * npair;
+      const int r = sigma - paired, u = r / nstage;
+      p = r - u * nstage;
+      ti = 2 * npair + u;
     }
   };
 
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
         u32x4 st[kHC];
         if (kPost) {
           const int row = min(T * kStatsRows + lrow, M - 1);
-          const float* cf = L.coef[ti & 3][lrow];
+          const float* cf = L.coef[ti & 1][lrow];
           float pj[kHC], cij[kHC][kHC];
 #pragma unroll
           for (int j = 0; j < kHC; ++j) pj[j] = cf[j];
@@ -310,11 +315,11 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
       for (int sub = 0; sub < 4; ++sub) v[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
     zero(aD0), zero(aD1), zero(aSq), zero(bD0), zero(bD1), zero(bSq);
-    // post / comb of tile iteration ti's 64 rows into coefficient slot ti & 3 (fused form)
+    // post / comb of tile iteration ti's 64 rows into coefficient slot ti & 1 (fused form)
     auto load_coef = [&](int ti) __attribute__((always_inline)) {
       if (ti >= my_tiles) return;  // block-uniform
       const int T = kb + ti * a.blocks_per_slice;
-      float* dst = &L.coef[ti & 3][0][0];
+      float* dst = &L.coef[ti & 1][0][0];
       for (int v = threadIdx.x - 256; v < kStatsRows * 5; v += 256) {
         const int lr = v / 5, k = v - lr * 5;
         const int row = min(T * kStatsRows + lr, M - 1);
@@ -396,24 +401,18 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
         pending = ti;  // flushed in the next iteration, after the barrier
       }
     };
-    // start of iteration i: the coefficients of the tile pair after the one whose stages the
-    // producers start now (fused form), and the flush of a finished tile
+    // start of iteration i: the coefficients of the tile after the one whose stages the
+    // producers start now (fused form, where tiles are not paired), and the flush of a
+    // finished tile
     auto begin = [&](int i) __attribute__((always_inline)) {
-      if (kPost && i < paired && i % (2 * nstage) == 0) {
-        const int k = i / (2 * nstage);
-        load_coef(2 * k + 2);
-        load_coef(2 * k + 3);
-      }
+      if (kPost && i % nstage == 0) load_coef(i / nstage + 1);
       if (pending >= 0) {
         flush(pending);
         pending = -1;
       }
     };
 
-    if (kPost) {
-      load_coef(0);
-      load_coef(1);
-    }
+    if (kPost) load_coef(0);
     __syncthreads();  // matches the producers' prologue barrier
     // Iteration i multiplies stage i - 1 (written by the producers in iteration i - 1) and ends
     // with the block barrier. Operands: a paired stage couple (2u, 2u + 1) shares the buffer of
@@ -444,7 +443,8 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
     if (paired > 0) mma(paired - 1, bY, bD0, bD1, bSq);
     load_b(paired + 1, bY);
     __syncthreads();
-    // the lone tile's stages (none when the tile count is even); total - paired is even
+    // the unpaired stages: the lone tile of the paired form, all tiles of the fused form
+    // (total - paired is even)
     for (int i = paired + 1; i <= total; i += 2) {
       begin(i);
       mma(i - 1, bX, aD0, aD1, aSq);
