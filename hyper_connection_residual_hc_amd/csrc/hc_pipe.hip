@@ -22,9 +22,12 @@
 //    lines), compute R' in the fused form, store it, and write the bf16 stage into one slot of
 //    a two-slot LDS ring; their loads run four stages ahead;
 //  * waves 4-7 (consumers) multiply the previous stage: consumer q owns stream q (2 chunks of
-//    32 columns) for all 64 rows, so one fn operand load serves 64 rows;
+//    32 columns) for all 64 rows, so one fn operand load serves 64 rows (128 when two tiles
+//    share their stages, see the stage schedule);
 //  * one block barrier per stage. Producer and consumer waves keep separate in-order load
-//    counters, so waiting for fn operands never waits for HBM.
+//    counters, so a consumer's wait for its fn operands does not count the producers' HBM
+//    loads (the operands, L2 hits, can still return behind HBM loads the CU issued earlier,
+//    which is why they are loaded two stages ahead).
 // The LDS tile stores 16-byte unit u of row r at unit u ^ (r & 15): the consumers' 16-byte
 // reads of 16 rows hit 16 distinct bank groups.
 //
