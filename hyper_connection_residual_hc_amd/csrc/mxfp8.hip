@@ -5,21 +5,21 @@
 // smallest e with amax * 2^-e <= 448), scale byte e + 127; elements y * 2^-e (exact in fp32)
 // rounded to nearest even into e4m3fn, saturating at +-448, with the sign of zero kept.
 //
-// One lane per 8 consecutive values (a 16-byte load, an 8-byte store of codes), eight such
-// units in flight per lane: a lane quad holds a 32-value block, whose maximum comes from a
-// quad DPP max; the quad's first lane writes the scale byte.
+// One lane per 8 consecutive values (a 16-byte load, an 8-byte store of codes), T such units
+// in flight per lane: a lane quad holds a 32-value block, whose maximum comes from a quad DPP
+// max; the quad's first lane writes the scale byte. T is 5 when a row's units come in
+// multiples of 320 (K = 5120: two full waves per row), else 8.
 #include "hc_launch.h"
 
 namespace hc {
 
-constexpr int kMxUnits = 8;  // 16-byte loads in flight per lane
-
+template <int T>
 __global__ __launch_bounds__(256) void mxfp8_kernel(const uint16_t* __restrict__ y, int64_t ldY,
                                                     int M, int U, int chunks,
                                                     uint8_t* __restrict__ q, int64_t ldQ,
                                                     uint8_t* __restrict__ sc, int64_t ldS) {
   // A unit is 8 consecutive values of a row; U = K / 8 units per row, a multiple of 4. A wave
-  // takes 512 units of one row (chunk j): lane l holds units 512 j + 64 t + l, t < 8, so each
+  // takes 64 T units of one row (chunk j): lane l holds units 64 (T j + t) + l, t < T, so each
   // load instruction reads 1 KB contiguous and the lane quads hold whole 32-value blocks.
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -27,15 +27,15 @@ __global__ __launch_bounds__(256) void mxfp8_kernel(const uint16_t* __restrict__
   if (m >= M) return;  // wave-uniform
   const int j = (int)(wid - (int64_t)m * chunks);
   const uint16_t* yr = y + (int64_t)m * ldY;
-  u32x4 v[kMxUnits];
+  u32x4 v[T];
 #pragma unroll
-  for (int t = 0; t < kMxUnits; ++t) {
-    const int u = 512 * j + 64 * t + lane;
+  for (int t = 0; t < T; ++t) {
+    const int u = 64 * (T * j + t) + lane;
     v[t] = ld16_stream(yr + 8 * (int64_t)min(u, U - 1));  // past the row's end: a valid unit
   }
 #pragma unroll
-  for (int t = 0; t < kMxUnits; ++t) {
-    const int u = 512 * j + 64 * t + lane;  // quads past the end are whole quads (U % 4 == 0)
+  for (int t = 0; t < T; ++t) {
+    const int u = 64 * (T * j + t) + lane;  // quads past the end are whole quads (U % 4 == 0)
     const int e = mx_block_exponent(quad_max_u32(amax_bits8(v[t])));
     if (u < U) {
       const float inv = mx_inv_scale(e);
@@ -51,10 +51,16 @@ __global__ __launch_bounds__(256) void mxfp8_kernel(const uint16_t* __restrict__
 hipError_t launch_mxfp8(const uint16_t* y, int64_t ldY, int M, int K, uint8_t* q, int64_t ldQ,
                         uint8_t* scales, int64_t ldS, hipStream_t s) {
   const int U = K / 8;
-  const int chunks = (U + 64 * kMxUnits - 1) / (64 * kMxUnits);
+  const int T = U % 320 == 0 ? 5 : 8;
+  const int chunks = (U + 64 * T - 1) / (64 * T);
   const int64_t waves = (int64_t)M * chunks;
-  hipLaunchKernelGGL(mxfp8_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, y, ldY,
-                     M, U, chunks, q, ldQ, scales, ldS);
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  if (T == 5)
+    hipLaunchKernelGGL(mxfp8_kernel<5>, grid, block, 0, s, y, ldY, M, U, chunks, q, ldQ, scales,
+                       ldS);
+  else
+    hipLaunchKernelGGL(mxfp8_kernel<8>, grid, block, 0, s, y, ldY, M, U, chunks, q, ldQ, scales,
+                       ldS);
   return hipGetLastError();
 }
 
