@@ -117,3 +117,12 @@ def test_config4_prefill_chunk_post_pre_mxfp8(sites):
     yo = torch.from_numpy(ref2["y_bits"].view(np.int16)).view(torch.bfloat16)
     q2, s2 = ops.mxfp8_quant_rows(gu.dev(yo))
     assert np.array_equal(q2.cpu().numpy(), oq) and np.array_equal(s2.cpu().numpy(), osf)
+
+    # the fused form of the same chunk (hc_post_pre_mxfp8: R', the pre and the MXFP8 epilogue
+    # in two launches) gives the unfused chain's bytes, at the full chunk size
+    R1f, (yf, qf, sff, post2f, comb2f, _) = ops.post_pre_mxfp8(
+        xd, Rd, post0, comb0, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d)
+    assert torch.equal(R1f.view(torch.int16), R1.view(torch.int16))
+    assert torch.equal(yf.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(qf, q) and torch.equal(sff, sf)
+    assert torch.equal(post2f, post2) and torch.equal(comb2f, comb2)
