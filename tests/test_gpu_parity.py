@@ -366,6 +366,37 @@ def test_wider_hidden_sizes(Hs):
     assert torch.equal(full[2], post2) and torch.equal(full[3], comb2)
 
 
+def test_narrowest_hidden_size_two_stages_per_slice():
+    """H = 1024: each slice is two stages, the fewest the stats kernels take, so tiles end on
+    every other stage (back-to-back epilogues; in the stats-only form the two tiles of a pair
+    end on consecutive stages). At M = 6161 every block runs several tiles (pairs and a lone
+    tile; in the fused form tiles one after another): the pre vs the oracle on sampled rows,
+    and the fused op vs post then pre, bit for bit."""
+    Hs, M = 1024, 6161
+    gu.say(f"H={Hs} M={M}")
+    site = gu.Site(21, 22, H_=Hs)
+    nxt = gu.Site(23, 24, H_=Hs)
+    R = inputs.residual(M, 25, H=Hs)
+    Rd = gu.dev(R)
+    y, post, comb, pre = ops.pre(Rd, site.fnp, site.scale_d, site.base_d, site.w_d,
+                                 want_pre=True)
+    rng = np.random.default_rng(6161)
+    rows = np.unique(np.concatenate([np.arange(70), np.arange(M - 70, M),
+                                     rng.choice(M, 200, replace=False)]))
+    ref = site.oracle_pre(inputs.bits(R)[rows])
+    ridx = torch.from_numpy(rows).to(gu.DEV)
+    gu.assert_coef_close(gu.f32_np(comb[ridx]), ref["comb"], "comb")
+    gu.assert_coef_close(gu.f32_np(pre[ridx]), ref["pre"], "pre")
+    gu.assert_bf16_close(gu.bits_of(y[ridx]), ref["y"], "y")
+    x = gu.dev(inputs.sublayer_out(M, 26, H=Hs))
+    full = ops.post_pre(x, Rd, post, comb, nxt.fnp, nxt.scale_d, nxt.base_d, nxt.w_d)
+    Rn = ops.post(x, Rd, post, comb)
+    y2, post2, comb2, _ = ops.pre(Rn, nxt.fnp, nxt.scale_d, nxt.base_d, nxt.w_d)
+    assert torch.equal(full[0].view(torch.int16), Rn.view(torch.int16))
+    assert torch.equal(full[1].view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(full[2], post2) and torch.equal(full[3], comb2)
+
+
 def test_graph_capture_replays_match_eager(attn, ffn):
     """The fused step captured in a HIP graph (the entry points allocate nothing and clear no
     memory, so they capture as plain kernel nodes): three replays, with unrelated eager work
