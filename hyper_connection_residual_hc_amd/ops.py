@@ -352,6 +352,7 @@ def pre_finish(R: torch.Tensor, workspace: torch.Tensor, scale: torch.Tensor,
     _contig(comb_o, "comb", torch.float32, (M, HC, HC))
     if pre_o is not None:
         _contig(pre_o, "pre", torch.float32, (M, HC))
+    _workspace(0, dev, workspace)  # a contiguous tensor: its byte count is its extent
     _one_device(R, workspace, scale, base, weight, y, post_o, comb_o, pre_o)
     _lib.call("hc_pre_finish", R.data_ptr(), ldR, scale.data_ptr(), base.data_ptr(),
               weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult,
@@ -455,6 +456,7 @@ def pre_finish_mxfp8(R: torch.Tensor, workspace: torch.Tensor, scale: torch.Tens
     _contig(base, "base", torch.float32, (MIX,))
     _contig(weight, "weight", torch.bfloat16, (H,))
     out = _mx_outputs(M, H, R.device, want_y, want_pre, out)
+    _workspace(0, R.device, workspace)  # a contiguous tensor: its byte count is its extent
     _one_device(R, workspace, scale, base, weight, *[t for t in out if t is not None])
     _lib.call("hc_pre_finish_mxfp8", R.data_ptr(), ldR, scale.data_ptr(), base.data_ptr(),
               weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult,

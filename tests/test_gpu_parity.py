@@ -339,6 +339,12 @@ def test_binding_rejects_short_outputs(attn, ffn):
                 workspace=torch.empty(ops.pre_workspace_bytes(M, gu.H), dtype=torch.uint8))
     with pytest.raises(ValueError):  # so would a host weight
         ops.combine_norm(R, post, attn.w_d.cpu())
+    R1, ws = ops.post_stats(x, R, post, comb, ffn.fnp)
+    spread = torch.empty(2 * ws.numel(), dtype=torch.uint8, device=R.device)
+    with pytest.raises(ValueError):  # a strided workspace: its byte count is not its extent
+        ops.pre_finish(R1, spread[::2], ffn.scale_d, ffn.base_d, ffn.w_d)
+    with pytest.raises(ValueError):
+        ops.pre_finish_mxfp8(R1, spread[::2], ffn.scale_d, ffn.base_d, ffn.w_d)
 
 
 @pytest.mark.parametrize("Hs", [2048, 7168, 8192])
