@@ -158,7 +158,8 @@ HC_API int mxfp8_quant_rows(const uint16_t* y, int64_t ldY, int64_t M, int32_t K
  * hc_pre_stats -> hc_sinkhorn -> hc_combine_norm.
  *
  * pre may be NULL (not written); post fp32 [M, 4], comb fp32 [M, 4, 4], y bf16 [M, H] (ldY).
- * H: as hc_combine_norm and a multiple of 1024. workspace: >= hc_pre_workspace_bytes(M, H).
+ * H: as hc_combine_norm and a multiple of 1024. workspace: >= hc_pre_workspace_bytes(M, H),
+ * 256-byte aligned (HC_ERR_ALIGN otherwise).
  * ------------------------------------------------------------------------------------- */
 HC_API size_t hc_pre_workspace_bytes(int64_t M, int32_t H);
 HC_API int hc_pre(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed,
@@ -182,7 +183,8 @@ HC_API int hc_pre(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed,
  * contiguous and 16-byte aligned; fn_packed / scale / base / weight: the next site's, as
  * for hc_pre. Rout: bf16 [M, 4, H] (ldOut); y: bf16 [M, H] (ldY); pre_out (or NULL),
  * post_out fp32 [M, 4], comb_out fp32 [M, 4, 4]: written. H: as hc_pre.
- * workspace: >= hc_post_pre_workspace_bytes(M, H). Outputs must not overlap any input.
+ * workspace: >= hc_post_pre_workspace_bytes(M, H), 256-byte aligned (HC_ERR_ALIGN otherwise).
+ * Outputs must not overlap any input.
  * ------------------------------------------------------------------------------------- */
 HC_API size_t hc_post_pre_workspace_bytes(int64_t M, int32_t H);
 HC_API int hc_post_pre(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
