@@ -443,3 +443,50 @@ def test_graph_capture_replays_match_eager(attn, ffn):
             if a.dtype == torch.bfloat16:
                 a, b = a.view(torch.int16), b.view(torch.int16)
             assert torch.equal(a, b), (rep, k)
+
+
+
+def _wide_bf16(M, inner, pad):
+    """(whole [M, inner + pad] buffer filled with -7, the [M, inner] view of its row heads)."""
+    b = torch.full((M, inner + pad), -7.0, dtype=torch.bfloat16, device=gu.DEV)
+    return b, b[:, :inner]
+
+
+def test_padded_row_strides_fused_and_separate(attn, ffn):
+    """Every bf16 row argument of hc_pre, hc_post and hc_post_pre as a view into wider rows
+    (a different pad for each), at a size where blocks run two and three 64-row tiles and the
+    last one is ragged: the same bits as the contiguous calls, and no pad byte written."""
+    M, H = 4177, gu.H
+    gu.say(f"padded strides M={M}")
+    R = gu.dev(inputs.residual(M, 91))
+    x = gu.dev(inputs.sublayer_out(M, 92))
+    y_c, post_c, comb_c, _ = ops.pre(R, attn.fnp, attn.scale_d, attn.base_d, attn.w_d)
+    ref_post = ops.post(x, R, post_c, comb_c)
+    ref = ops.post_pre(x, R, post_c, comb_c, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d)
+
+    Rb, Rv = _wide_bf16(M, 4 * H, 512)
+    Rv.copy_(R.reshape(M, 4 * H))
+    Rs = Rv.view(M, 4, H)
+    xb, xs = _wide_bf16(M, H, 64)
+    xs.copy_(x)
+    Rb0, xb0 = Rb.clone(), xb.clone()
+
+    yb, ys = _wide_bf16(M, H, 128)
+    y2, post2, comb2, _ = ops.pre(Rs, attn.fnp, attn.scale_d, attn.base_d, attn.w_d,
+                                  out=(ys, _poison_f32(M, 4), _poison_f32(M, 4, 4), None))
+    assert torch.equal(y2, y_c) and torch.equal(post2, post_c) and torch.equal(comb2, comb_c)
+    assert bool((yb[:, H:] == -7.0).all())
+
+    ob, ov = _wide_bf16(M, 4 * H, 256)
+    assert torch.equal(ops.post(xs, Rs, post_c, comb_c, out=ov.view(M, 4, H)), ref_post)
+    assert bool((ob[:, 4 * H:] == -7.0).all())
+
+    Rnb, Rnv = _wide_bf16(M, 4 * H, 1024)
+    ynb, ynv = _wide_bf16(M, H, 32)
+    got = ops.post_pre(xs, Rs, post_c, comb_c, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d,
+                       out=(Rnv.view(M, 4, H), ynv, _poison_f32(M, 4), _poison_f32(M, 4, 4),
+                            None))
+    for a, b, what in zip(got[:4], ref[:4], ("R'", "y", "post", "comb")):
+        assert torch.equal(a, b), what
+    assert bool((Rnb[:, 4 * H:] == -7.0).all()) and bool((ynb[:, H:] == -7.0).all())
+    assert torch.equal(Rb, Rb0) and torch.equal(xb, xb0)  # inputs, pads included, untouched
