@@ -490,3 +490,35 @@ def test_padded_row_strides_fused_and_separate(attn, ffn):
         assert torch.equal(a, b), what
     assert bool((Rnb[:, 4 * H:] == -7.0).all()) and bool((ynb[:, H:] == -7.0).all())
     assert torch.equal(Rb, Rb0) and torch.equal(xb, xb0)  # inputs, pads included, untouched
+
+
+def test_full_size_post_pre_matches_oracle_on_sampled_rows(attn, ffn):
+    """The measured step itself: hc_post_pre at M = 4096, H = 5120 in the launch the throughput
+    benchmark times (256 blocks of two 64-row tiles each), against the oracle's post followed by
+    its pre on sampled rows: every tile's first and last row, the first and last 70 rows, and
+    200 drawn at random. post and comb come from the oracle's pre of the attention site."""
+    M = 4096
+    gu.say(f"hc_post_pre full size M={M} sampled")
+    R = inputs.residual(M, 4096 + 11)
+    x = inputs.sublayer_out(M, 4096 + 12)
+    ref1 = attn.oracle_pre(inputs.bits(R))
+    post32 = torch.from_numpy(ref1["post"].astype(np.float32))
+    comb32 = torch.from_numpy(ref1["comb"].astype(np.float32))
+    Rn, y, post2, comb2, pre2 = ops.post_pre(
+        gu.dev(x), gu.dev(R), gu.dev(post32), gu.dev(comb32), ffn.fnp, ffn.scale_d,
+        ffn.base_d, ffn.w_d, want_pre=True,
+        out=(_poison_bf16(M, 4, gu.H), _poison_bf16(M, gu.H), _poison_f32(M, 4),
+             _poison_f32(M, 4, 4), _poison_f32(M, 4)))
+    rng = np.random.default_rng(4096)
+    edges = np.concatenate([np.arange(0, M, 64), np.arange(63, M, 64)])
+    rows = np.unique(np.concatenate([edges, np.arange(70), np.arange(M - 70, M),
+                                     rng.choice(M, 200, replace=False)]))
+    oR1, oR1_bits = o.hc_post(inputs.bits(x)[rows], inputs.bits(R)[rows], post32.numpy()[rows],
+                              comb32.numpy()[rows])
+    ref2 = ffn.oracle_pre(oR1_bits)
+    ridx = torch.from_numpy(rows).to(gu.DEV)
+    gu.assert_bf16_close(gu.bits_of(Rn[ridx]), oR1, "R' (sampled)")
+    gu.assert_bf16_close(gu.bits_of(y[ridx]), ref2["y"], "y (sampled)")
+    for name, g in (("pre", pre2), ("post", post2), ("comb", comb2)):
+        err = np.abs(gu.f32_np(g[ridx]) - ref2[name]).max()
+        assert err <= 2e-3, f"{name} (sampled): {err}"
