@@ -175,6 +175,66 @@ def ops_table(args, sets, fnp, sc, ba, w, torch, ops, inputs, d) -> int:
     return 0
 
 
+def decode_table(args, torch, ops, inputs, d) -> int:
+    """Decode-sized batches (the decode and verify steps run hc pre / post on a few rows): GPU
+    time per call of hc_pre, hc_post_pre, hc_post and hc_head at M = 1 .. 16, measured as a HIP
+    graph of back-to-back calls replayed (so the host's launch cost is not in it), one JSON line
+    per (entry point, M)."""
+    dev = torch.device("cuda:0")
+    fn_a, sc_a, ba_a = map(d, inputs.hc_params(inputs.SEED_ATTN))
+    fn_f, sc_f, ba_f = map(d, inputs.hc_params(inputs.SEED_FFN))
+    w_a = d(inputs.norm_weight(inputs.SEED_NORM_ATTN))
+    w_f = d(inputs.norm_weight(inputs.SEED_NORM_FFN))
+    fnp_a, fnp_f = ops.fn_pack(fn_a), ops.fn_pack(fn_f)
+    fh, sh, bh = map(d, inputs.hc_head_params(inputs.SEED_HEAD))
+    fnp_h = ops.head_fn_pack(fh)
+    calls = 50
+
+    def graph_us(fn_):
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                fn_()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(calls):
+                fn_()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, args.steps // 20)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * calls)
+
+    for M in (1, 2, 4, 8, 16):
+        R = d(inputs.residual(M, M))
+        x = d(inputs.sublayer_out(M, M + 1))
+        _, post, comb, _ = ops.pre(R, fnp_a, sc_a, ba_a, w_a)
+        R1 = torch.empty_like(R)
+        y = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
+        po, co = torch.empty(M, HC, device=dev), torch.empty(M, HC, HC, device=dev)
+        ws = torch.empty(max(ops.pre_workspace_bytes(M, H), ops.post_pre_workspace_bytes(M, H)),
+                         dtype=torch.uint8, device=dev)
+        table = {
+            "hc_pre": lambda: ops.pre(R, fnp_f, sc_f, ba_f, w_f, out=(y, po, co, None),
+                                      workspace=ws),
+            "hc_post_pre": lambda: ops.post_pre(x, R, post, comb, fnp_f, sc_f, ba_f, w_f,
+                                                out=(R1, y, po, co, None), workspace=ws),
+            "hc_post": lambda: ops.post(x, R, post, comb, out=R1),
+            "hc_head": lambda: ops.head(R, fnp_h, sh, bh, out=y, workspace=ws),
+        }
+        for name, fn_ in table.items():
+            print(json.dumps({"op": name, "M": M, "H": H, "us_per_call_graph": graph_us(fn_)}),
+                  flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +248,9 @@ def main() -> int:
                     help="instead of the step: time every entry point alone at M=4096 and print "
                          "one JSON line per entry point (wall clock per call; run it under "
                          "rocprofv3 --kernel-trace for kernel durations)")
+    ap.add_argument("--decode", action="store_true",
+                    help="instead of the step: GPU time per call of the decode-sized calls "
+                         "(M = 1 .. 16) from HIP graph replays, one JSON line each")
     ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
                     help="fused: hc_post_pre (post with the next pre's mix stats in one pass, "
                          "then the pre finish); unfused: hc_post then hc_pre")
@@ -207,6 +270,8 @@ def main() -> int:
         build.build()
     dev = torch.device("cuda:0")
     d = lambda t: t.to(dev).contiguous()  # noqa: E731
+    if args.decode:
+        return decode_table(args, torch, ops, inputs, d)
 
     fn_a, sc_a, ba_a = map(d, inputs.hc_params(inputs.SEED_ATTN))
     fn_f, sc_f, ba_f = map(d, inputs.hc_params(inputs.SEED_FFN))

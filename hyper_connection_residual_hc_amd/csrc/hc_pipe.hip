@@ -462,6 +462,150 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
   }
 }
 
+// ---- decode-sized batches -----------------------------------------------------------------------
+// The decode and verify steps run the decoder layer's hc pre and post on a handful of rows
+// (the engine gates its fused combine-norm on 1..8 rows as on long prefill chunks;
+// prefill_sp.py, _combine_norm_fused). For up to 16 rows (one MFMA row tile) the pipelined
+// kernel is latency-bound: it runs its ten-stage pipeline over a 64-row tile whatever the row
+// count. pipe_small_kernel writes the same partials for such batches in one pass: block s is
+// slice s and wave q is stream q; each wave walks its stream's chunks of the slice in the
+// pipelined kernel's order (stage p, then half hq, i.e. chunk c = 2p + hq), with the same A and
+// B operands and the same sequence of MFMAs into the same three accumulators, and the four
+// streams' accumulators are added in the same order through LDS. Every partial, and so every
+// output of the path, is bit-identical to what pipe_kernel gives for these rows, so a call's
+// bits do not depend on which kernel its row count selects (a row slice of a large call gives
+// the large call's bits).
+//
+// The block first stages its slice of x (R, or in the fused form R' formed from R and the
+// sublayer output with the producers' operation order, and stored) for all rows in LDS, rows
+// padded by 16 bytes so that the MFMA operand reads of 8 rows hit distinct banks; the fn
+// operand loads of the first kSmallAhead chunks are issued before it, so both latencies overlap.
+constexpr int kSmallRows = 16;
+constexpr int kSmallAhead = 16;
+
+inline int small_row_elems(int H) { return H / kSlices + 8; }
+inline size_t small_lds_bytes(int H) {
+  return (size_t)kHC * kSmallRows * small_row_elems(H) * 2 + (size_t)kHC * kSmallRows * kEpiCols * 4;
+}
+constexpr size_t kSmallLdsMax = 150 * 1024;
+
+template <bool kPost>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void pipe_small_kernel(PipeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char small_lds[];
+  const int M = a.M, H = a.H;
+  const int W = H / kSlices;               // slice width (columns of each stream)
+  const int LR = W + 8;                    // LDS row stride in elements
+  uint16_t* xs = reinterpret_cast<uint16_t*>(small_lds);  // [4 streams][16 rows][LR]
+  float(*ep)[kSmallRows][kEpiCols] =
+      reinterpret_cast<float(*)[kSmallRows][kEpiCols]>(small_lds + (size_t)kHC * kSmallRows * LR * 2);
+  const int s = blockIdx.x;                // slice
+  const int q = threadIdx.x >> 6;          // stream of this wave's MFMAs
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nch = 2 * (W / kPipeH);        // chunks of one stream in a slice (multiple of 4)
+  const int hs = s * W;
+  const u32x4* bq = reinterpret_cast<const u32x4*>(a.fnp) +
+                    (int64_t)s * chunks_per_slice(H) * kPackTiles * 64 + lane;
+  u32x4 fb[kSmallAhead][kPackTiles];
+  auto issue = [&](int c, u32x4 (&d)[kPackTiles]) __attribute__((always_inline)) {
+    const int p = c >> 1, hq = c & 1;
+#pragma unroll
+    for (int t = 0; t < kPackTiles; ++t)
+      d[t] = bq[((int64_t)(p * kStageChunks + 2 * q + hq) * kPackTiles + t) * 64];
+  };
+#pragma unroll
+  for (int u = 0; u < kSmallAhead; ++u)
+    if (u < nch) issue(u, fb[u]);
+
+  // stage the slice: item = (row, 8-column group), groups of a row on consecutive threads
+  const int groups = W / 8;
+  for (int it = threadIdx.x; it < M * groups; it += 256) {
+    const int r = it / groups;
+    const int h = hs + 8 * (it - r * groups);
+    const uint16_t* Rr = a.R + (int64_t)r * a.ldR + h;
+    u32x4 v[kHC];
+    if (kPost) {
+      u32x4 rv[kHC];
+#pragma unroll
+      for (int i = 0; i < kHC; ++i) rv[i] = ld16(Rr + (int64_t)i * H);
+      const u32x4 xv = ld16(a.x + (int64_t)r * a.ldX + h);
+      float xf[8], rf[kHC][8];
+      unpack8(xv, xf);
+#pragma unroll
+      for (int i = 0; i < kHC; ++i) unpack8(rv[i], rf[i]);
+      const float* cf = a.comb + (int64_t)r * kHC * kHC;
+#pragma unroll
+      for (int j = 0; j < kHC; ++j) {
+        const float pj = a.post[(int64_t)r * kHC + j];
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float acc = pj * xf[e];
+#pragma unroll
+          for (int i = 0; i < kHC; ++i) acc = __fmaf_rn(cf[i * kHC + j], rf[i][e], acc);
+          o[e] = acc;
+        }
+        v[j] = pack8(o);
+        st16(a.out + (int64_t)r * a.ldOut + (int64_t)j * H + h, v[j]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kHC; ++i) v[i] = ld16(Rr + (int64_t)i * H);
+    }
+#pragma unroll
+    for (int i = 0; i < kHC; ++i)
+      *reinterpret_cast<u32x4*>(&xs[((size_t)i * kSmallRows + r) * LR + (h - hs)]) = v[i];
+  }
+  __syncthreads();
+
+  // rows past the end repeat row M-1 (their results are not written)
+  const uint16_t* arow = xs + ((size_t)q * kSmallRows + min(r16, M - 1)) * LR + 8 * g;
+  f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0, sq = d0;
+  for (int c0 = 0; c0 < nch; c0 += kSmallAhead) {
+#pragma unroll
+    for (int u = 0; u < kSmallAhead; ++u) {
+      const int c = c0 + u;
+      if (c < nch) {
+        const bf16x8 xa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow + 32 * c));
+        const u32x4(&b)[kPackTiles] = fb[u];
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[0]), d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[3]), d1, 0, 0, 0);
+        sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, xa, sq, 0, 0, 0);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[1]), d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[4]), d1, 0, 0, 0);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[2]), d0, 0, 0, 0);
+        if (c + kSmallAhead < nch) issue(c + kSmallAhead, fb[u]);
+      }
+    }
+  }
+  // the pipelined kernel's epilogue layout: lane holds rows 4g + i of column r16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ep[q][4 * g + i][r16] = d0[i];
+    ep[q][4 * g + i][16 + r16] = d1[i];
+    if (r16 == 4 * g + i) ep[q][r16][32] = sq[i];
+  }
+  __syncthreads();
+  // and its flush: streams added in order, f 16..23 as (hi + lo) + mid
+  for (int idx = threadIdx.x; idx < M * (kMix + 1); idx += 256) {
+    const int r = idx / (kMix + 1);
+    const int f = idx - r * (kMix + 1);
+    float v = 0.0f;
+    if (f < 16) {
+#pragma unroll
+      for (int w = 0; w < kHC; ++w) v += ep[w][r][f];
+    } else if (f < kMix) {
+#pragma unroll
+      for (int w = 0; w < kHC; ++w) v += ep[w][r][f] + ep[w][r][f + 8];
+    } else {
+#pragma unroll
+      for (int w = 0; w < kHC; ++w) v += ep[w][r][32];
+    }
+    a.part[((int64_t)s * M + r) * kPartStride + f] = v;
+  }
+}
+
 static int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
@@ -474,7 +618,33 @@ static int device_cus() {
   return cus[dev];
 }
 
+// The decode-sized kernel takes more than 64 KB of dynamic LDS: allow it once per device.
+static bool small_kernel_ready() {
+  static signed char ok[64] = {0};  // 0 unknown, 1 ready, -1 failed
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (ok[dev] == 0) {
+    const int bytes = (int)kSmallLdsMax;
+    const bool good =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&pipe_small_kernel<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&pipe_small_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess;
+    ok[dev] = good ? 1 : -1;
+  }
+  return ok[dev] > 0;
+}
+
 static hipError_t launch_pipe(bool fused, PipeArgs args, hipStream_t s) {
+  const size_t small_lds = small_lds_bytes(args.H);
+  if (args.M >= 1 && args.M <= kSmallRows && small_lds <= kSmallLdsMax && small_kernel_ready()) {
+    // decode-sized: same bits in one pass (H up to 8192 fits the slice in LDS)
+    if (fused)
+      hipLaunchKernelGGL(pipe_small_kernel<true>, dim3(kSlices), dim3(256), small_lds, s, args);
+    else
+      hipLaunchKernelGGL(pipe_small_kernel<false>, dim3(kSlices), dim3(256), small_lds, s, args);
+    return hipGetLastError();
+  }
   args.tiles = (args.M + kStatsRows - 1) / kStatsRows;
   args.blocks_per_slice = max(1, min(args.tiles, device_cus() / kSlices));
   const dim3 grid((unsigned)(args.blocks_per_slice * kSlices)), block(512);

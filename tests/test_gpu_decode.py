@@ -1,0 +1,92 @@
+"""Decode-sized batches: 1 to 16 rows take the mix stats through a one-pass kernel instead of the
+pipelined one (the decode and verify steps of the decoder layer run hc pre / post on a few rows;
+prefill_sp.py, _combine_norm_fused gates the engine's fused combine-norm on 1..8 rows). Its
+partials, and so every output, must be the pipelined kernel's bits, or a row slice of a large
+call would differ from the large call. Checked here as row slices of 80-row calls (which take
+the pipelined kernel: a full 64-row tile and a ragged one) at four hidden sizes (8192 the
+largest whose slice the one-pass kernel stages in LDS), for every
+entry point that computes mix stats, and against the oracle at decode sizes."""
+import numpy as np
+import pytest
+import torch
+
+from hyper_connection_residual_hc_amd import inputs, ops
+from oracle import hc_oracle as o
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+M_BIG = 80
+# slices of 1..16 rows: both tiles, tile boundaries, odd offsets, the last row
+SLICES = [(0, 1), (0, 16), (3, 5), (7, 15), (31, 39), (48, 64), (63, 65), (64, 80), (70, 77),
+          (79, 80)]
+
+
+def _eq(a, b):
+    if a.dtype == torch.bfloat16:
+        a, b = a.view(torch.int16), b.view(torch.int16)
+    return torch.equal(a, b)
+
+
+@pytest.mark.parametrize("H", [5120, 1024, 7168, 8192])
+def test_decode_sized_slices_match_the_pipelined_kernel(H):
+    gu.say(f"decode-sized slices H={H}")
+    attn = gu.Site(inputs.SEED_ATTN, inputs.SEED_NORM_ATTN, H_=H)
+    ffn = gu.Site(inputs.SEED_FFN, inputs.SEED_NORM_FFN, H_=H)
+    fh, sh, bh = inputs.hc_head_params(inputs.SEED_HEAD, H=H)
+    hfnp, sh, bh = ops.head_fn_pack(gu.dev(fh)), gu.dev(sh), gu.dev(bh)
+    R = gu.dev(inputs.residual(M_BIG, M_BIG, H=H))
+    x = gu.dev(inputs.sublayer_out(M_BIG, M_BIG + 1, H=H))
+    _, post, comb, _ = ops.pre(R, attn.fnp, attn.scale_d, attn.base_d, attn.w_d)
+
+    def run(sl):
+        Rs, xs, ps, cs = R[sl], x[sl], post[sl], comb[sl]
+        pp = ops.post_pre(xs, Rs, ps, cs, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d,
+                          want_pre=True)
+        ppm = ops.post_pre_mxfp8(xs, Rs, ps, cs, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d,
+                                 want_y=False)
+        R1, ws = ops.post_stats(xs, Rs, ps, cs, ffn.fnp)
+        return {
+            "pre_stats": ops.pre_stats(Rs, ffn.fnp),
+            "pre": ops.pre(Rs, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d, want_pre=True),
+            "pre_mxfp8": ops.pre_mxfp8(Rs, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d),
+            "post_pre": pp,
+            "post_pre_mxfp8": ppm,
+            "halves": (R1,) + ops.pre_finish(R1, ws, ffn.scale_d, ffn.base_d, ffn.w_d),
+            "head": (ops.head(Rs, hfnp, sh, bh),),
+        }
+
+    full = run(slice(0, M_BIG))
+    for lo, hi in SLICES:
+        got = run(slice(lo, hi))
+        for name, outs in got.items():
+            for k, (g, f) in enumerate(zip(outs, full[name])):
+                if g is None or not isinstance(g, torch.Tensor):
+                    continue
+                assert _eq(g, f[lo:hi]), f"H={H} {name}[{k}] differs on rows [{lo}, {hi})"
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_decode_sized_post_pre_matches_oracle(M):
+    """hc post (attention site) then hc pre (FFN site) at decode sizes against the oracle."""
+    gu.say(f"decode-sized post_pre vs oracle M={M}")
+    attn = gu.Site(inputs.SEED_ATTN, inputs.SEED_NORM_ATTN)
+    ffn = gu.Site(inputs.SEED_FFN, inputs.SEED_NORM_FFN)
+    R_h = inputs.residual(M, 7 + M)
+    x_h = inputs.sublayer_out(M, 8 + M)
+    R, x = gu.dev(R_h), gu.dev(x_h)
+    _, post, comb, _ = ops.pre(R, attn.fnp, attn.scale_d, attn.base_d, attn.w_d)
+    R1, y, post2, comb2, pre2 = ops.post_pre(x, R, post, comb, ffn.fnp, ffn.scale_d,
+                                             ffn.base_d, ffn.w_d, want_pre=True)
+    mixes = ops.pre_stats(R1, ffn.fnp)[0]
+    # post against the oracle on the GPU's own coefficients
+    oR1, _ = o.hc_post(inputs.bits(x_h), inputs.bits(R_h), gu.f32_np(post).astype(np.float32),
+                       gu.f32_np(comb).astype(np.float32))
+    gu.assert_bf16_close(gu.bits_of(R1), oR1, "R'")
+    # pre against the oracle on the GPU's R'
+    ref = ffn.oracle_pre(gu.bits_of(R1))
+    gu.assert_mixes_close(gu.f32_np(mixes), ref["mixes"])
+    gu.assert_coef_close(gu.f32_np(pre2), ref["pre"], "pre")
+    gu.assert_coef_close(gu.f32_np(post2), ref["post"], "post")
+    gu.assert_coef_close(gu.f32_np(comb2), ref["comb"], "comb")
+    gu.assert_bf16_close(gu.bits_of(y), ref["y"], "y")
