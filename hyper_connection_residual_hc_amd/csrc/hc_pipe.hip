@@ -113,8 +113,13 @@ __global__ __launch_bounds__(256) void fn_pack_kernel(const float* __restrict__ 
   st16(out + gid * 8, pack8(v));  // the parts are exact bf16 values: packing does not round
 }
 
+static bool small_kernel_ready();
+
 hipError_t launch_fn_pack(const float* fn, int H, int rows, uint16_t* fn_packed,
                           hipStream_t s) {
+  // Packing runs before any stats call, normally eagerly at set-up: allow the decode-sized
+  // kernel its LDS here, so that the first decode call never does it inside a graph capture.
+  (void)small_kernel_ready();
   const int64_t total = (int64_t)kSlices * chunks_per_slice(H) * kPackTiles * 64;
   hipLaunchKernelGGL(fn_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, fn,
                      H, rows, fn_packed);
@@ -630,6 +635,7 @@ static bool small_kernel_ready() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess &&
         hipFuncSetAttribute(reinterpret_cast<const void*>(&pipe_small_kernel<false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess;
+    if (!good) (void)hipGetLastError();  // the pipelined kernel serves instead: no error left
     ok[dev] = good ? 1 : -1;
   }
   return ok[dev] > 0;

@@ -90,3 +90,67 @@ def test_decode_sized_post_pre_matches_oracle(M):
     gu.assert_coef_close(gu.f32_np(post2), ref["post"], "post")
     gu.assert_coef_close(gu.f32_np(comb2), ref["comb"], "comb")
     gu.assert_bf16_close(gu.bits_of(y), ref["y"], "y")
+
+
+def test_decode_sized_graph_replays_and_padded_strides():
+    """hc_post_pre at 7 rows captured in a HIP graph: three replays, with eager work and a
+    synchronisation between them, each give the eager bits; and every bf16 row argument as a
+    view into wider rows gives the contiguous call's bits and writes no pad byte."""
+    gu.say("decode-sized graph replays and padded strides M=7")
+    M, H = 7, gu.H
+    attn = gu.Site(inputs.SEED_ATTN, inputs.SEED_NORM_ATTN)
+    ffn = gu.Site(inputs.SEED_FFN, inputs.SEED_NORM_FFN)
+    R = gu.dev(inputs.residual(M, 41))
+    x = gu.dev(inputs.sublayer_out(M, 42))
+    _, post, comb, _ = ops.pre(R, attn.fnp, attn.scale_d, attn.base_d, attn.w_d)
+    outs = (torch.empty_like(R), torch.empty(M, H, dtype=torch.bfloat16, device=gu.DEV),
+            torch.empty(M, 4, device=gu.DEV), torch.empty(M, 4, 4, device=gu.DEV), None)
+    ws = torch.empty(ops.post_pre_workspace_bytes(M, H), dtype=torch.uint8, device=gu.DEV)
+
+    def step():
+        ops.post_pre(x, R, post, comb, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d, out=outs,
+                     workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs[:4]]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = gu.dev(inputs.residual(M, 43))
+    for rep in range(3):
+        for t in outs[:4]:
+            t.view(torch.uint8).fill_(0xA5)
+        ops.pre(other, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d)  # eager work in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(outs[:4], ref)):
+            assert _eq(a, b), (rep, k)
+
+    # padded row strides: R, x, R' and y as views into wider rows, each with its own pad
+    def wide(inner, pad, src=None):
+        b = torch.full((M, inner + pad), -7.0, dtype=torch.bfloat16, device=gu.DEV)
+        v = b[:, :inner]
+        if src is not None:
+            v.copy_(src.reshape(M, inner))
+        return b, v
+
+    Rb, Rv = wide(4 * H, 512, R)
+    xb, xv = wide(H, 256, x)
+    R1b, R1v = wide(4 * H, 1024)
+    yb, yv = wide(H, 128)
+    got = ops.post_pre(xv, Rv.view(M, 4, H), post, comb, ffn.fnp, ffn.scale_d, ffn.base_d,
+                       ffn.w_d, out=(R1v.view(M, 4, H), yv, torch.empty_like(outs[2]),
+                                     torch.empty_like(outs[3]), None))
+    torch.cuda.synchronize()
+    assert _eq(R1v.reshape(M, 4, H), ref[0]) and _eq(yv, ref[1])
+    assert _eq(got[2], ref[2]) and _eq(got[3], ref[3])
+    for b, inner in ((R1b, 4 * H), (yb, H)):
+        assert bool((b[:, inner:] == -7.0).all()), "a pad byte was written"
