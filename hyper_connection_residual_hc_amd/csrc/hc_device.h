@@ -165,20 +165,26 @@ __device__ __forceinline__ int mx_block_exponent(uint32_t amax_bits) {
   return min(max(e, -127), 127);
 }
 
-// 2^-e as fp32, exact for e in [-127, 126] (finite bf16 maxima give e <= 120).
-__device__ __forceinline__ float mx_inv_scale(int e) {
-  return __uint_as_float((uint32_t)(127 - e) << 23);
+// The block scale 2^e as the divisor the MX conversion takes: the scale byte e + 127 in the
+// fp32 exponent field. The conversion reads only that field, so byte 0 (e = -127) stands for
+// 2^-127 as in the ue8m0 format, although as an fp32 it is 0.
+__device__ __forceinline__ float mx_scale(int e) {
+  return __uint_as_float((uint32_t)(e + 127) << 23);
 }
 
-// Four bf16 values in two packed words, w0 = (v0, v1) and w1 = (v2, v3), scaled by inv (a
-// power of two) -> four e4m3fn codes in one word, v0 in the low byte: the matrix-core-era
-// conversion v_cvt_pk_fp8_f32 (OCP e4m3fn on gfx950), round to nearest even, sign of zero
-// kept, subnormals down to 2^-9. Its overflow result is NaN rather than +-448, which the MX
-// scale rule never reaches: every scaled value is at most 448.
-__device__ __forceinline__ uint32_t e4m3_word(uint32_t w0, uint32_t w1, float inv) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(bf_lo(w0) * inv, bf_hi(w0) * inv, 0, false);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(bf_lo(w1) * inv, bf_hi(w1) * inv, r, true);
-  return (uint32_t)r;
+// Four bf16 values in two packed words, w0 = (v0, v1) and w1 = (v2, v3), divided by the block
+// scale -> four e4m3fn codes in one word, v0 in the low byte: CDNA4's MX conversion
+// v_cvt_scalef32_pk_fp8_bf16 (OCP e4m3fn), which takes the bf16 pair as it is, scales it
+// exactly by the power of two and rounds to nearest even, keeping the sign of zero, subnormals
+// down to 2^-9. Its results equal those of an fp32 multiply by 2^-e and v_cvt_pk_fp8_f32 for
+// every finite bf16 and every e that leaves the value in range; the MX scale rule keeps every
+// scaled value within +-448, so nothing overflows.
+__device__ __forceinline__ uint32_t e4m3_word(uint32_t w0, uint32_t w1, float scale) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  s16x2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, w0), scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, w1), scale, true);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // Largest magnitude bits (low 15 bits) of 8 packed bf16.

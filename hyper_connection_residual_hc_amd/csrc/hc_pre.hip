@@ -123,10 +123,10 @@ __device__ __forceinline__ void combine_norm_row(const RowTile<NG>& t, const flo
     if (!kMx || yr) st16_stream(yr + g * 512 + lane * 8, yb);
     if constexpr (kMx) {
       const int ex = mx_block_exponent(quad_max_u32(amax_bits8(yb)));
-      const float inv = mx_inv_scale(ex);
+      const float scl = mx_scale(ex);
       u32x2 codes;
-      codes[0] = e4m3_word(yb[0], yb[1], inv);
-      codes[1] = e4m3_word(yb[2], yb[3], inv);
+      codes[0] = e4m3_word(yb[0], yb[1], scl);
+      codes[1] = e4m3_word(yb[2], yb[3], scl);
       __builtin_nontemporal_store(codes, reinterpret_cast<u32x2*>(qr + g * 512 + lane * 8));
       if ((lane & 3) == 0) sr[g * 16 + (lane >> 2)] = (uint8_t)(ex + 127);
     }

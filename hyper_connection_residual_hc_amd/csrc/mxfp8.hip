@@ -2,8 +2,9 @@
 // mxfp8_gather: e4m3 elements with one ue8m0 scale per row per 32 columns, linear scales).
 //
 // Per 32-column block: the block exponent e from the largest |y| (mx_block_exponent: the
-// smallest e with amax * 2^-e <= 448), scale byte e + 127; elements y * 2^-e (exact in fp32)
-// rounded to nearest even into e4m3fn, saturating at +-448, with the sign of zero kept.
+// smallest e with amax * 2^-e <= 448), scale byte e + 127; elements y * 2^-e (an exact
+// power-of-two scaling) rounded to nearest even into e4m3fn, with the sign of zero kept; the
+// rule keeps every scaled value within +-448.
 //
 // One lane per 8 consecutive values (a 16-byte load, an 8-byte store of codes), T such units
 // in flight per lane: a lane quad holds a 32-value block, whose maximum comes from a quad DPP
@@ -38,10 +39,10 @@ __global__ __launch_bounds__(256) void mxfp8_kernel(const uint16_t* __restrict__
     const int u = 64 * (T * j + t) + lane;  // quads past the end are whole quads (U % 4 == 0)
     const int e = mx_block_exponent(quad_max_u32(amax_bits8(v[t])));
     if (u < U) {
-      const float inv = mx_inv_scale(e);
+      const float scl = mx_scale(e);
       u32x2 codes;
-      codes[0] = e4m3_word(v[t][0], v[t][1], inv);
-      codes[1] = e4m3_word(v[t][2], v[t][3], inv);
+      codes[0] = e4m3_word(v[t][0], v[t][1], scl);
+      codes[1] = e4m3_word(v[t][2], v[t][3], scl);
       __builtin_nontemporal_store(codes, reinterpret_cast<u32x2*>(q + (int64_t)m * ldQ + 8 * (int64_t)u));
       if ((u & 3) == 0) sc[(int64_t)m * ldS + (u >> 2)] = (uint8_t)(e + 127);
     }
