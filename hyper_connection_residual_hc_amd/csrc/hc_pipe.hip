@@ -473,20 +473,24 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
 // prefill_sp.py, _combine_norm_fused). For up to 16 rows (one MFMA row tile) the pipelined
 // kernel is latency-bound: it runs its ten-stage pipeline over a 64-row tile whatever the row
 // count. pipe_small_kernel writes the same partials for such batches in one pass: block s is
-// slice s and wave q is stream q; each wave walks its stream's chunks of the slice in the
-// pipelined kernel's order (stage p, then half hq, i.e. chunk c = 2p + hq), with the same A and
-// B operands and the same sequence of MFMAs into the same three accumulators, and the four
-// streams' accumulators are added in the same order through LDS. Every partial, and so every
-// output of the path, is bit-identical to what pipe_kernel gives for these rows, so a call's
-// bits do not depend on which kernel its row count selects (a row slice of a large call gives
-// the large call's bits).
+// slice s and wave q < 4 is stream q; each of those waves walks its stream's chunks of the
+// slice in the pipelined kernel's order (stage p, then half hq, i.e. chunk c = 2p + hq), with
+// the same A and B operands and the same sequence of MFMAs into the same three accumulators,
+// and the four streams' accumulators are added in the same order through LDS. Every partial,
+// and so every output of the path, is bit-identical to what pipe_kernel gives for these rows,
+// so a call's bits do not depend on which kernel its row count selects (a row slice of a large
+// call gives the large call's bits).
 //
-// The block first stages its slice of x (R, or in the fused form R' formed from R and the
-// sublayer output with the producers' operation order, and stored) for all rows in LDS, rows
-// padded by 16 bytes so that the MFMA operand reads of 8 rows hit distinct banks; the fn
-// operand loads of the first kSmallAhead chunks are issued before it, so both latencies overlap.
+// The block's 8 waves first stage its slice of x (R, or in the fused form R' formed from R and
+// the sublayer output with the producers' operation order, and stored) for all rows in LDS, rows
+// padded by 16 bytes so that the MFMA operand reads of 8 rows hit distinct banks; waves 0-3
+// issue the fn operand loads of their first kSmallAhead chunks before it, so both latencies
+// overlap. (Two waves per SIMD halve the staging arithmetic's time; a deeper fn window, 16
+// chunks on one wave per SIMD, measured no faster.)
 constexpr int kSmallRows = 16;
-constexpr int kSmallAhead = 16;
+constexpr int kSmallAhead = 8;
+constexpr int kStageBatch = 2;
+constexpr int kSmallThreads = 512;  // all 8 waves stage the slice; waves 0-3 run the MFMAs
 
 inline int small_row_elems(int H) { return H / kSlices + 8; }
 inline size_t small_lds_bytes(int H) {
@@ -495,8 +499,7 @@ inline size_t small_lds_bytes(int H) {
 constexpr size_t kSmallLdsMax = 150 * 1024;
 
 template <bool kPost>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void pipe_small_kernel(PipeArgs a) {
+__global__ __launch_bounds__(kSmallThreads) void pipe_small_kernel(PipeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char small_lds[];
   const int M = a.M, H = a.H;
   const int W = H / kSlices;               // slice width (columns of each stream)
@@ -505,7 +508,7 @@ void pipe_small_kernel(PipeArgs a) {
   float(*ep)[kSmallRows][kEpiCols] =
       reinterpret_cast<float(*)[kSmallRows][kEpiCols]>(small_lds + (size_t)kHC * kSmallRows * LR * 2);
   const int s = blockIdx.x;                // slice
-  const int q = threadIdx.x >> 6;          // stream of this wave's MFMAs
+  const int q = threadIdx.x >> 6;          // waves 0-3: the stream of this wave's MFMAs
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const int nch = 2 * (W / kPipeH);        // chunks of one stream in a slice (multiple of 4)
@@ -519,81 +522,103 @@ void pipe_small_kernel(PipeArgs a) {
     for (int t = 0; t < kPackTiles; ++t)
       d[t] = bq[((int64_t)(p * kStageChunks + 2 * q + hq) * kPackTiles + t) * 64];
   };
+  const bool mma_wave = q < kHC;  // wave-uniform
+  if (mma_wave) {
 #pragma unroll
-  for (int u = 0; u < kSmallAhead; ++u)
-    if (u < nch) issue(u, fb[u]);
+    for (int u = 0; u < kSmallAhead; ++u)
+      if (u < nch) issue(u, fb[u]);
+  }
 
-  // stage the slice: item = (row, 8-column group), groups of a row on consecutive threads
+  // stage the slice: item = (row, 8-column group), groups of a row on consecutive threads; the
+  // loads of kStageBatch items per thread go out together
   const int groups = W / 8;
-  for (int it = threadIdx.x; it < M * groups; it += 256) {
-    const int r = it / groups;
-    const int h = hs + 8 * (it - r * groups);
-    const uint16_t* Rr = a.R + (int64_t)r * a.ldR + h;
-    u32x4 v[kHC];
-    if (kPost) {
-      u32x4 rv[kHC];
+  const int items = M * groups;
+  constexpr int kLoads = kPost ? kHC + 1 : kHC;  // R's streams (and the sublayer output)
+  for (int it0 = threadIdx.x; it0 < items; it0 += kSmallThreads * kStageBatch) {
+    u32x4 ld[kStageBatch][kLoads];
 #pragma unroll
-      for (int i = 0; i < kHC; ++i) rv[i] = ld16(Rr + (int64_t)i * H);
-      const u32x4 xv = ld16(a.x + (int64_t)r * a.ldX + h);
-      float xf[8], rf[kHC][8];
-      unpack8(xv, xf);
+    for (int bi = 0; bi < kStageBatch; ++bi) {
+      const int it = it0 + kSmallThreads * bi;
+      if (it < items) {
+        const int r = it / groups;
+        const int h = hs + 8 * (it - r * groups);
+        const uint16_t* Rr = a.R + (int64_t)r * a.ldR + h;
 #pragma unroll
-      for (int i = 0; i < kHC; ++i) unpack8(rv[i], rf[i]);
-      const float* cf = a.comb + (int64_t)r * kHC * kHC;
-#pragma unroll
-      for (int j = 0; j < kHC; ++j) {
-        const float pj = a.post[(int64_t)r * kHC + j];
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float acc = pj * xf[e];
-#pragma unroll
-          for (int i = 0; i < kHC; ++i) acc = __fmaf_rn(cf[i * kHC + j], rf[i][e], acc);
-          o[e] = acc;
-        }
-        v[j] = pack8(o);
-        st16(a.out + (int64_t)r * a.ldOut + (int64_t)j * H + h, v[j]);
+        for (int i = 0; i < kHC; ++i) ld[bi][i] = ld16(Rr + (int64_t)i * H);
+        if (kPost) ld[bi][kLoads - 1] = ld16(a.x + (int64_t)r * a.ldX + h);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kHC; ++i) v[i] = ld16(Rr + (int64_t)i * H);
     }
 #pragma unroll
-    for (int i = 0; i < kHC; ++i)
-      *reinterpret_cast<u32x4*>(&xs[((size_t)i * kSmallRows + r) * LR + (h - hs)]) = v[i];
+    for (int bi = 0; bi < kStageBatch; ++bi) {
+      const int it = it0 + kSmallThreads * bi;
+      if (it < items) {
+        const int r = it / groups;
+        const int h = hs + 8 * (it - r * groups);
+        u32x4 v[kHC];
+        if (kPost) {
+          float xf[8], rf[kHC][8];
+          unpack8(ld[bi][kLoads - 1], xf);
+#pragma unroll
+          for (int i = 0; i < kHC; ++i) unpack8(ld[bi][i], rf[i]);
+          const float* cf = a.comb + (int64_t)r * kHC * kHC;
+#pragma unroll
+          for (int j = 0; j < kHC; ++j) {
+            const float pj = a.post[(int64_t)r * kHC + j];
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float acc = pj * xf[e];
+#pragma unroll
+              for (int i = 0; i < kHC; ++i) acc = __fmaf_rn(cf[i * kHC + j], rf[i][e], acc);
+              o[e] = acc;
+            }
+            v[j] = pack8(o);
+            st16(a.out + (int64_t)r * a.ldOut + (int64_t)j * H + h, v[j]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < kHC; ++i) v[i] = ld[bi][i];
+        }
+#pragma unroll
+        for (int i = 0; i < kHC; ++i)
+          *reinterpret_cast<u32x4*>(&xs[((size_t)i * kSmallRows + r) * LR + (h - hs)]) = v[i];
+      }
+    }
   }
   __syncthreads();
 
-  // rows past the end repeat row M-1 (their results are not written)
-  const uint16_t* arow = xs + ((size_t)q * kSmallRows + min(r16, M - 1)) * LR + 8 * g;
-  f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0, sq = d0;
-  for (int c0 = 0; c0 < nch; c0 += kSmallAhead) {
+  if (mma_wave) {
+    // rows past the end repeat row M-1 (their results are not written)
+    const uint16_t* arow = xs + ((size_t)q * kSmallRows + min(r16, M - 1)) * LR + 8 * g;
+    f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0, sq = d0;
+    for (int c0 = 0; c0 < nch; c0 += kSmallAhead) {
 #pragma unroll
-    for (int u = 0; u < kSmallAhead; ++u) {
-      const int c = c0 + u;
-      if (c < nch) {
-        const bf16x8 xa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow + 32 * c));
-        const u32x4(&b)[kPackTiles] = fb[u];
-        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[0]), d0, 0, 0, 0);
-        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[3]), d1, 0, 0, 0);
-        sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, xa, sq, 0, 0, 0);
-        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[1]), d0, 0, 0, 0);
-        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[4]), d1, 0, 0, 0);
-        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[2]), d0, 0, 0, 0);
-        if (c + kSmallAhead < nch) issue(c + kSmallAhead, fb[u]);
+      for (int u = 0; u < kSmallAhead; ++u) {
+        const int c = c0 + u;
+        if (c < nch) {
+          const bf16x8 xa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow + 32 * c));
+          const u32x4(&b)[kPackTiles] = fb[u];
+          d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[0]), d0, 0, 0, 0);
+          d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[3]), d1, 0, 0, 0);
+          sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, xa, sq, 0, 0, 0);
+          d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[1]), d0, 0, 0, 0);
+          d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[4]), d1, 0, 0, 0);
+          d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, b[2]), d0, 0, 0, 0);
+          if (c + kSmallAhead < nch) issue(c + kSmallAhead, fb[u]);
+        }
       }
     }
-  }
-  // the pipelined kernel's epilogue layout: lane holds rows 4g + i of column r16
+    // the pipelined kernel's epilogue layout: lane holds rows 4g + i of column r16
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ep[q][4 * g + i][r16] = d0[i];
-    ep[q][4 * g + i][16 + r16] = d1[i];
-    if (r16 == 4 * g + i) ep[q][r16][32] = sq[i];
+    for (int i = 0; i < 4; ++i) {
+      ep[q][4 * g + i][r16] = d0[i];
+      ep[q][4 * g + i][16 + r16] = d1[i];
+      if (r16 == 4 * g + i) ep[q][r16][32] = sq[i];
+    }
   }
   __syncthreads();
   // and its flush: streams added in order, f 16..23 as (hi + lo) + mid
-  for (int idx = threadIdx.x; idx < M * (kMix + 1); idx += 256) {
+  for (int idx = threadIdx.x; idx < M * (kMix + 1); idx += kSmallThreads) {
     const int r = idx / (kMix + 1);
     const int f = idx - r * (kMix + 1);
     float v = 0.0f;
@@ -646,9 +671,11 @@ static hipError_t launch_pipe(bool fused, PipeArgs args, hipStream_t s) {
   if (args.M >= 1 && args.M <= kSmallRows && small_lds <= kSmallLdsMax && small_kernel_ready()) {
     // decode-sized: same bits in one pass (H up to 8192 fits the slice in LDS)
     if (fused)
-      hipLaunchKernelGGL(pipe_small_kernel<true>, dim3(kSlices), dim3(256), small_lds, s, args);
+      hipLaunchKernelGGL(pipe_small_kernel<true>, dim3(kSlices), dim3(kSmallThreads), small_lds, s,
+                         args);
     else
-      hipLaunchKernelGGL(pipe_small_kernel<false>, dim3(kSlices), dim3(256), small_lds, s, args);
+      hipLaunchKernelGGL(pipe_small_kernel<false>, dim3(kSlices), dim3(kSmallThreads), small_lds, s,
+                         args);
     return hipGetLastError();
   }
   args.tiles = (args.M + kStatsRows - 1) / kStatsRows;
