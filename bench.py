@@ -175,11 +175,11 @@ def ops_table(args, sets, fnp, sc, ba, w, torch, ops, inputs, d) -> int:
     return 0
 
 
-def decode_table(args, torch, ops, inputs, d) -> int:
-    """Decode-sized batches (the decode and verify steps run hc pre / post on a few rows): GPU
-    time per call of hc_pre, hc_post_pre, hc_post and hc_head at M = 1 .. 16, measured as a HIP
-    graph of back-to-back calls replayed (so the host's launch cost is not in it), one JSON line
-    per (entry point, M)."""
+def small_table(args, torch, ops, inputs, d) -> int:
+    """Small batches (decode and verify steps run hc pre / post on a few rows, short prefill
+    chunks on a few hundred): GPU time per call of hc_pre, hc_post_pre, hc_post and hc_head at
+    M = 1 .. 1024, measured as a HIP graph of back-to-back calls replayed (so the host's launch
+    cost is not in it), one JSON line per (entry point, M)."""
     dev = torch.device("cuda:0")
     fn_a, sc_a, ba_a = map(d, inputs.hc_params(inputs.SEED_ATTN))
     fn_f, sc_f, ba_f = map(d, inputs.hc_params(inputs.SEED_FFN))
@@ -212,7 +212,7 @@ def decode_table(args, torch, ops, inputs, d) -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / (reps * calls)
 
-    for M in (1, 2, 4, 8, 16):
+    for M in (1, 2, 4, 8, 16, 64, 256, 1024):
         R = d(inputs.residual(M, M))
         x = d(inputs.sublayer_out(M, M + 1))
         _, post, comb, _ = ops.pre(R, fnp_a, sc_a, ba_a, w_a)
@@ -248,9 +248,9 @@ def main() -> int:
                     help="instead of the step: time every entry point alone at M=4096 and print "
                          "one JSON line per entry point (wall clock per call; run it under "
                          "rocprofv3 --kernel-trace for kernel durations)")
-    ap.add_argument("--decode", action="store_true",
-                    help="instead of the step: GPU time per call of the decode-sized calls "
-                         "(M = 1 .. 16) from HIP graph replays, one JSON line each")
+    ap.add_argument("--small", action="store_true",
+                    help="instead of the step: GPU time per call of small batches "
+                         "(M = 1 .. 1024) from HIP graph replays, one JSON line each")
     ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
                     help="fused: hc_post_pre (post with the next pre's mix stats in one pass, "
                          "then the pre finish); unfused: hc_post then hc_pre")
@@ -270,8 +270,8 @@ def main() -> int:
         build.build()
     dev = torch.device("cuda:0")
     d = lambda t: t.to(dev).contiguous()  # noqa: E731
-    if args.decode:
-        return decode_table(args, torch, ops, inputs, d)
+    if args.small:
+        return small_table(args, torch, ops, inputs, d)
 
     fn_a, sc_a, ba_a = map(d, inputs.hc_params(inputs.SEED_ATTN))
     fn_f, sc_f, ba_f = map(d, inputs.hc_params(inputs.SEED_FFN))

@@ -117,7 +117,7 @@ static bool small_kernel_ready();
 
 hipError_t launch_fn_pack(const float* fn, int H, int rows, uint16_t* fn_packed,
                           hipStream_t s) {
-  // Packing runs before any stats call, normally eagerly at set-up: allow the decode-sized
+  // Packing runs before any stats call, normally eagerly at set-up: allow the small-batch
   // kernel its LDS here, so that the first decode call never does it inside a graph capture.
   (void)small_kernel_ready();
   const int64_t total = (int64_t)kSlices * chunks_per_slice(H) * kPackTiles * 64;
@@ -467,19 +467,21 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
   }
 }
 
-// ---- decode-sized batches -----------------------------------------------------------------------
+// ---- small batches (decode, verify, short prefill) -----------------------------------------------
 // The decode and verify steps run the decoder layer's hc pre and post on a handful of rows
 // (the engine gates its fused combine-norm on 1..8 rows as on long prefill chunks;
-// prefill_sp.py, _combine_norm_fused). For up to 16 rows (one MFMA row tile) the pipelined
-// kernel is latency-bound: it runs its ten-stage pipeline over a 64-row tile whatever the row
-// count. pipe_small_kernel writes the same partials for such batches in one pass: block s is
-// slice s and wave q < 4 is stream q; each of those waves walks its stream's chunks of the
-// slice in the pipelined kernel's order (stage p, then half hq, i.e. chunk c = 2p + hq), with
-// the same A and B operands and the same sequence of MFMAs into the same three accumulators,
-// and the four streams' accumulators are added in the same order through LDS. Every partial,
-// and so every output of the path, is bit-identical to what pipe_kernel gives for these rows,
-// so a call's bits do not depend on which kernel its row count selects (a row slice of a large
-// call gives the large call's bits).
+// prefill_sp.py, _combine_norm_fused). Below about a thousand rows the pipelined kernel is
+// latency-bound: each block runs a ten-stage pipeline over one or a few 64-row tiles.
+// pipe_small_kernel writes the same partials for such batches in one pass per 16-row group
+// (one MFMA row tile): block b takes slice b % 8 (so the blocks of a slice share an XCD and its
+// L2 copy of the slice's packed fn) and rows [16 (b / 8), +16); wave q < 4 is stream q. Each
+// of those waves walks its stream's chunks of the slice in the pipelined kernel's order (stage
+// p, then half hq, i.e. chunk c = 2p + hq), with the same A and B operands and the same
+// sequence of MFMAs into the same three accumulators, and the four streams' accumulators are
+// added in the same order through LDS. Every partial, and so every output of the path, is
+// bit-identical to what pipe_kernel gives for these rows, so a call's bits do not depend on
+// which kernel its row count selects (a row slice of a large call gives the large call's
+// bits). Above about 1024 rows the pipelined kernel is faster (measured crossover).
 //
 // The block's 8 waves first stage its slice of x (R, or in the fused form R' formed from R and
 // the sublayer output with the producers' operation order, and stored) for all rows in LDS, rows
@@ -487,7 +489,8 @@ __global__ __launch_bounds__(512) void pipe_kernel(PipeArgs a) {
 // issue the fn operand loads of their first kSmallAhead chunks before it, so both latencies
 // overlap. (Two waves per SIMD halve the staging arithmetic's time; a deeper fn window, 16
 // chunks on one wave per SIMD, measured no faster.)
-constexpr int kSmallRows = 16;
+constexpr int kSmallRows = 16;        // rows of one block (one MFMA row tile)
+constexpr int kSmallMaxRows = 1024;   // largest batch the one-pass kernel takes
 constexpr int kSmallAhead = 8;
 constexpr int kStageBatch = 2;
 constexpr int kSmallThreads = 512;  // all 8 waves stage the slice; waves 0-3 run the MFMAs
@@ -507,7 +510,9 @@ __global__ __launch_bounds__(kSmallThreads) void pipe_small_kernel(PipeArgs a) {
   uint16_t* xs = reinterpret_cast<uint16_t*>(small_lds);  // [4 streams][16 rows][LR]
   float(*ep)[kSmallRows][kEpiCols] =
       reinterpret_cast<float(*)[kSmallRows][kEpiCols]>(small_lds + (size_t)kHC * kSmallRows * LR * 2);
-  const int s = blockIdx.x;                // slice
+  const int s = blockIdx.x % kSlices;      // slice: the blocks of a slice share an XCD's L2
+  const int r0 = (blockIdx.x / kSlices) * kSmallRows;  // this block's 16-row group
+  const int Mg = min(kSmallRows, M - r0);  // its rows
   const int q = threadIdx.x >> 6;          // waves 0-3: the stream of this wave's MFMAs
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
@@ -532,7 +537,7 @@ __global__ __launch_bounds__(kSmallThreads) void pipe_small_kernel(PipeArgs a) {
   // stage the slice: item = (row, 8-column group), groups of a row on consecutive threads; the
   // loads of kStageBatch items per thread go out together
   const int groups = W / 8;
-  const int items = M * groups;
+  const int items = Mg * groups;
   constexpr int kLoads = kPost ? kHC + 1 : kHC;  // R's streams (and the sublayer output)
   for (int it0 = threadIdx.x; it0 < items; it0 += kSmallThreads * kStageBatch) {
     u32x4 ld[kStageBatch][kLoads];
@@ -542,10 +547,10 @@ __global__ __launch_bounds__(kSmallThreads) void pipe_small_kernel(PipeArgs a) {
       if (it < items) {
         const int r = it / groups;
         const int h = hs + 8 * (it - r * groups);
-        const uint16_t* Rr = a.R + (int64_t)r * a.ldR + h;
+        const uint16_t* Rr = a.R + (int64_t)(r0 + r) * a.ldR + h;
 #pragma unroll
         for (int i = 0; i < kHC; ++i) ld[bi][i] = ld16(Rr + (int64_t)i * H);
-        if (kPost) ld[bi][kLoads - 1] = ld16(a.x + (int64_t)r * a.ldX + h);
+        if (kPost) ld[bi][kLoads - 1] = ld16(a.x + (int64_t)(r0 + r) * a.ldX + h);
       }
     }
 #pragma unroll
@@ -560,10 +565,10 @@ __global__ __launch_bounds__(kSmallThreads) void pipe_small_kernel(PipeArgs a) {
           unpack8(ld[bi][kLoads - 1], xf);
 #pragma unroll
           for (int i = 0; i < kHC; ++i) unpack8(ld[bi][i], rf[i]);
-          const float* cf = a.comb + (int64_t)r * kHC * kHC;
+          const float* cf = a.comb + (int64_t)(r0 + r) * kHC * kHC;
 #pragma unroll
           for (int j = 0; j < kHC; ++j) {
-            const float pj = a.post[(int64_t)r * kHC + j];
+            const float pj = a.post[(int64_t)(r0 + r) * kHC + j];
             float o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -573,7 +578,7 @@ __global__ __launch_bounds__(kSmallThreads) void pipe_small_kernel(PipeArgs a) {
               o[e] = acc;
             }
             v[j] = pack8(o);
-            st16(a.out + (int64_t)r * a.ldOut + (int64_t)j * H + h, v[j]);
+            st16(a.out + (int64_t)(r0 + r) * a.ldOut + (int64_t)j * H + h, v[j]);
           }
         } else {
 #pragma unroll
@@ -589,7 +594,7 @@ __global__ __launch_bounds__(kSmallThreads) void pipe_small_kernel(PipeArgs a) {
 
   if (mma_wave) {
     // rows past the end repeat row M-1 (their results are not written)
-    const uint16_t* arow = xs + ((size_t)q * kSmallRows + min(r16, M - 1)) * LR + 8 * g;
+    const uint16_t* arow = xs + ((size_t)q * kSmallRows + min(r16, Mg - 1)) * LR + 8 * g;
     f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0, sq = d0;
     for (int c0 = 0; c0 < nch; c0 += kSmallAhead) {
 #pragma unroll
@@ -618,7 +623,7 @@ __global__ __launch_bounds__(kSmallThreads) void pipe_small_kernel(PipeArgs a) {
   }
   __syncthreads();
   // and its flush: streams added in order, f 16..23 as (hi + lo) + mid
-  for (int idx = threadIdx.x; idx < M * (kMix + 1); idx += kSmallThreads) {
+  for (int idx = threadIdx.x; idx < Mg * (kMix + 1); idx += kSmallThreads) {
     const int r = idx / (kMix + 1);
     const int f = idx - r * (kMix + 1);
     float v = 0.0f;
@@ -632,7 +637,7 @@ __global__ __launch_bounds__(kSmallThreads) void pipe_small_kernel(PipeArgs a) {
 #pragma unroll
       for (int w = 0; w < kHC; ++w) v += ep[w][r][32];
     }
-    a.part[((int64_t)s * M + r) * kPartStride + f] = v;
+    a.part[((int64_t)s * M + r0 + r) * kPartStride + f] = v;
   }
 }
 
@@ -648,7 +653,7 @@ static int device_cus() {
   return cus[dev];
 }
 
-// The decode-sized kernel takes more than 64 KB of dynamic LDS: allow it once per device.
+// The small-batch kernel takes more than 64 KB of dynamic LDS: allow it once per device.
 static bool small_kernel_ready() {
   static signed char ok[64] = {0};  // 0 unknown, 1 ready, -1 failed
   int dev = 0;
@@ -668,14 +673,13 @@ static bool small_kernel_ready() {
 
 static hipError_t launch_pipe(bool fused, PipeArgs args, hipStream_t s) {
   const size_t small_lds = small_lds_bytes(args.H);
-  if (args.M >= 1 && args.M <= kSmallRows && small_lds <= kSmallLdsMax && small_kernel_ready()) {
-    // decode-sized: same bits in one pass (H up to 8192 fits the slice in LDS)
+  if (args.M >= 1 && args.M <= kSmallMaxRows && small_lds <= kSmallLdsMax && small_kernel_ready()) {
+    // small batches: same bits in one pass per 16-row group (H up to 8192 fits a slice in LDS)
+    const dim3 grid((unsigned)(kSlices * ((args.M + kSmallRows - 1) / kSmallRows)));
     if (fused)
-      hipLaunchKernelGGL(pipe_small_kernel<true>, dim3(kSlices), dim3(kSmallThreads), small_lds, s,
-                         args);
+      hipLaunchKernelGGL(pipe_small_kernel<true>, grid, dim3(kSmallThreads), small_lds, s, args);
     else
-      hipLaunchKernelGGL(pipe_small_kernel<false>, dim3(kSlices), dim3(kSmallThreads), small_lds, s,
-                         args);
+      hipLaunchKernelGGL(pipe_small_kernel<false>, grid, dim3(kSmallThreads), small_lds, s, args);
     return hipGetLastError();
   }
   args.tiles = (args.M + kStatsRows - 1) / kStatsRows;

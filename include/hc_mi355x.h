@@ -19,9 +19,9 @@
  *   row pointer advanced by a rows and M = b - a; the library takes no "logical row count",
  *   and every row's result is bit-identical whether the row is computed in a full call or in
  *   any slice (mxfp8_swizzle_128x4, a layout over the whole of M, is the one exception). The
- *   one choice keyed on M is which kernel computes the mix stats: decode-sized calls (1 to 16
- *   rows, H up to 8192) take a one-pass kernel with lower latency whose results are the same
- *   bits as the pipelined kernel's.
+ *   one choice keyed on M is which kernel computes the mix stats: calls of up to 1024 rows
+ *   (decode, verify, short prefill; H up to 8192) take a one-pass kernel with lower latency
+ *   whose results are the same bits as the pipelined kernel's.
  * - Return value: HC_OK (0) or one of the HC_ERR_* codes below; hc_status_string() names it.
  *   An error return means nothing was enqueued.
  *

@@ -1,11 +1,12 @@
-"""Decode-sized batches: 1 to 16 rows take the mix stats through a one-pass kernel instead of the
-pipelined one (the decode and verify steps of the decoder layer run hc pre / post on a few rows;
+"""Small batches: calls of up to 1024 rows (decode, verify, short prefill) take the mix stats
+through a one-pass kernel, one block per (16-row group, slice), instead of the pipelined one
+(the decode and verify steps of the decoder layer run hc pre / post on a few rows;
 prefill_sp.py, _combine_norm_fused gates the engine's fused combine-norm on 1..8 rows). Its
 partials, and so every output, must be the pipelined kernel's bits, or a row slice of a large
-call would differ from the large call. Checked here as row slices of 80-row calls (which take
-the pipelined kernel: a full 64-row tile and a ragged one) at four hidden sizes (8192 the
-largest whose slice the one-pass kernel stages in LDS), for every
-entry point that computes mix stats, and against the oracle at decode sizes."""
+call would differ from the large call. Checked here as row slices of 1100-row calls (which
+take the pipelined kernel) at four hidden sizes (8192 the largest whose slice the one-pass
+kernel stages in LDS), for every entry point that computes mix stats, and against the oracle
+at small sizes."""
 import numpy as np
 import pytest
 import torch
@@ -16,10 +17,11 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-M_BIG = 80
-# slices of 1..16 rows: both tiles, tile boundaries, odd offsets, the last row
-SLICES = [(0, 1), (0, 16), (3, 5), (7, 15), (31, 39), (48, 64), (63, 65), (64, 80), (70, 77),
-          (79, 80)]
+M_BIG = 1100  # above the one-pass kernel's 1024 rows: the pipelined kernel
+# slices of 1 .. 1024 rows: one and several 16-row groups, ragged last groups, tile boundaries,
+# odd offsets, the last rows
+SLICES = [(0, 1), (0, 16), (3, 5), (7, 15), (31, 39), (48, 64), (63, 65), (1, 18), (70, 177),
+          (333, 433), (5, 1029), (76, 1100), (1099, 1100)]
 
 
 def _eq(a, b):
@@ -29,8 +31,8 @@ def _eq(a, b):
 
 
 @pytest.mark.parametrize("H", [5120, 1024, 7168, 8192])
-def test_decode_sized_slices_match_the_pipelined_kernel(H):
-    gu.say(f"decode-sized slices H={H}")
+def test_small_batch_slices_match_the_pipelined_kernel(H):
+    gu.say(f"small-batch slices H={H}")
     attn = gu.Site(inputs.SEED_ATTN, inputs.SEED_NORM_ATTN, H_=H)
     ffn = gu.Site(inputs.SEED_FFN, inputs.SEED_NORM_FFN, H_=H)
     fh, sh, bh = inputs.hc_head_params(inputs.SEED_HEAD, H=H)
@@ -66,10 +68,10 @@ def test_decode_sized_slices_match_the_pipelined_kernel(H):
                 assert _eq(g, f[lo:hi]), f"H={H} {name}[{k}] differs on rows [{lo}, {hi})"
 
 
-@pytest.mark.parametrize("M", [1, 5, 16])
-def test_decode_sized_post_pre_matches_oracle(M):
-    """hc post (attention site) then hc pre (FFN site) at decode sizes against the oracle."""
-    gu.say(f"decode-sized post_pre vs oracle M={M}")
+@pytest.mark.parametrize("M", [1, 5, 16, 100])
+def test_small_batch_post_pre_matches_oracle(M):
+    """hc post (attention site) then hc pre (FFN site) at small sizes against the oracle."""
+    gu.say(f"small-batch post_pre vs oracle M={M}")
     attn = gu.Site(inputs.SEED_ATTN, inputs.SEED_NORM_ATTN)
     ffn = gu.Site(inputs.SEED_FFN, inputs.SEED_NORM_FFN)
     R_h = inputs.residual(M, 7 + M)
@@ -92,11 +94,11 @@ def test_decode_sized_post_pre_matches_oracle(M):
     gu.assert_bf16_close(gu.bits_of(y), ref["y"], "y")
 
 
-def test_decode_sized_graph_replays_and_padded_strides():
+def test_small_batch_graph_replays_and_padded_strides():
     """hc_post_pre at 7 rows captured in a HIP graph: three replays, with eager work and a
     synchronisation between them, each give the eager bits; and every bf16 row argument as a
     view into wider rows gives the contiguous call's bits and writes no pad byte."""
-    gu.say("decode-sized graph replays and padded strides M=7")
+    gu.say("small-batch graph replays and padded strides M=7")
     M, H = 7, gu.H
     attn = gu.Site(inputs.SEED_ATTN, inputs.SEED_NORM_ATTN)
     ffn = gu.Site(inputs.SEED_FFN, inputs.SEED_NORM_FFN)
