@@ -34,7 +34,8 @@
 // Partials go to a workspace [8][M][32] (24 dots, sum of squares); consumers sum their four
 // streams' accumulators in stream order. Nothing depends on M or on where a row sits in its
 // tile (rows past the end recompute row M-1 and store identical bits), so any row slice of a
-// call gives the same bits as the full call.
+// call gives the same bits as the full call. Calls of up to 1024 rows take pipe_small_kernel
+// (end of this file) instead, which writes the same partials in one pass.
 #include "hc_launch.h"
 
 namespace hc {
@@ -118,7 +119,7 @@ static bool small_kernel_ready();
 hipError_t launch_fn_pack(const float* fn, int H, int rows, uint16_t* fn_packed,
                           hipStream_t s) {
   // Packing runs before any stats call, normally eagerly at set-up: allow the small-batch
-  // kernel its LDS here, so that the first decode call never does it inside a graph capture.
+  // kernel its LDS here, so that its first call never does it inside a graph capture.
   (void)small_kernel_ready();
   const int64_t total = (int64_t)kSlices * chunks_per_slice(H) * kPackTiles * 64;
   hipLaunchKernelGGL(fn_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, fn,
@@ -497,7 +498,8 @@ constexpr int kSmallThreads = 512;  // all 8 waves stage the slice; waves 0-3 ru
 
 inline int small_row_elems(int H) { return H / kSlices + 8; }
 inline size_t small_lds_bytes(int H) {
-  return (size_t)kHC * kSmallRows * small_row_elems(H) * 2 + (size_t)kHC * kSmallRows * kEpiCols * 4;
+  return (size_t)kHC * kSmallRows * small_row_elems(H) * 2 +
+         (size_t)kHC * kSmallRows * kEpiCols * 4;
 }
 constexpr size_t kSmallLdsMax = 150 * 1024;
 
