@@ -256,7 +256,7 @@ def main() -> int:
                          "then the pre finish); unfused: hc_post then hc_pre")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the mHC path is row-local and this build has no "
+        print("bench.py measures one GPU only: the mHC path is row-local and the library has no "
               "multi-GPU leg (rows would shard across GPUs with no exchange inside the path).",
               file=sys.stderr)
         return 2
