@@ -4,7 +4,7 @@ through a one-pass kernel, one block per (16-row group, slice), instead of the p
 prefill_sp.py, _combine_norm_fused gates the engine's fused combine-norm on 1..8 rows). Its
 partials, and so every output, must be the pipelined kernel's bits, or a row slice of a large
 call would differ from the large call. Checked here as row slices of 1100-row calls (which
-take the pipelined kernel) at four hidden sizes (8192 the largest whose slice the one-pass
+take the pipelined kernel) at six hidden sizes (8192 the largest whose slice the one-pass
 kernel stages in LDS), for every entry point that computes mix stats, and against the oracle
 at small sizes."""
 import numpy as np
@@ -30,7 +30,7 @@ def _eq(a, b):
     return torch.equal(a, b)
 
 
-@pytest.mark.parametrize("H", [5120, 1024, 7168, 8192])
+@pytest.mark.parametrize("H", [5120, 1024, 2048, 4096, 7168, 8192])
 def test_small_batch_slices_match_the_pipelined_kernel(H):
     gu.say(f"small-batch slices H={H}")
     attn = gu.Site(inputs.SEED_ATTN, inputs.SEED_NORM_ATTN, H_=H)
