@@ -187,12 +187,17 @@ def hc_post(x_bits, R_bits, post, comb):
 # pre (all of stages 1-4) and the chains
 # ------------------------------------------------------------------------------------------
 def hc_pre(R_bits, fn, scale, base, w_bits, rms_eps: float = RMS_EPS, hc_eps: float = HC_EPS,
-           iters: int = ITERS, post_mult: float = POST_MULT):
-    """Stages 1-4. Returns dict(mixes, sumsq, pre, post, comb, y, y_bits)."""
+           iters: int = ITERS, post_mult: float = POST_MULT, norm_eps: float = RMS_EPS):
+    """Stages 1-4. Returns dict(mixes, sumsq, pre, post, comb, y, y_bits).
+
+    Three eps values, each in its own stage as the decoder layer passes them (hc_pre's
+    TileLang call: rms_eps to the mix stats, hc_eps to pre and to the Sinkhorn, the norm
+    module's own variance epsilon to the RMSNorm after the combine); the model uses 1e-6
+    for all three."""
     hc = np.asarray(R_bits).shape[1]
     mixes, sumsq = hc_mix_stats(R_bits, fn, rms_eps)
     pre, post, comb = hc_split_sinkhorn(mixes, scale, base, hc, iters, hc_eps, post_mult)
-    y, y_bits = hc_combine_norm(R_bits, pre, w_bits, rms_eps)
+    y, y_bits = hc_combine_norm(R_bits, pre, w_bits, norm_eps)
     return dict(mixes=mixes, sumsq=sumsq, pre=pre, post=post, comb=comb, y=y, y_bits=y_bits)
 
 

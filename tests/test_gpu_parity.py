@@ -286,12 +286,18 @@ def test_fused_post_pre_matches_oracle(attn, ffn):
                                              ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d,
                                              want_pre=True)
     oR1, oR1_bits = o.hc_post(inputs.bits(x), inputs.bits(R), post32.numpy(), comb32.numpy())
-    ref2 = ffn.oracle_pre(oR1_bits)
     gu.assert_bf16_close(gu.bits_of(Rn), oR1, "R'")
-    gu.assert_bf16_close(gu.bits_of(y), ref2["y"], "y ffn")
+    # the pre half on the GPU's own R' bits: per-stage bars (coefficients 1e-5)
+    ref2g = ffn.oracle_pre(gu.bits_of(Rn))
+    gu.assert_bf16_close(gu.bits_of(y), ref2g["y"], "y ffn")
+    for name, g in (("pre", pre2), ("post", post2), ("comb", comb2)):
+        gu.assert_coef_close(gu.f32_np(g), ref2g[name], f"{name} ffn")
+    # and against the oracle's whole chain (its own R'), one bf16 rounding of R' apart
+    ref2 = ffn.oracle_pre(oR1_bits)
+    gu.assert_bf16_close(gu.bits_of(y), ref2["y"], "y ffn (oracle chain)")
     for name, g in (("pre", pre2), ("post", post2), ("comb", comb2)):
         err = np.abs(gu.f32_np(g) - ref2[name]).max()
-        assert err <= 2e-3, f"{name} ffn (chain): {err}"
+        assert err <= 2e-3, f"{name} ffn (oracle chain): {err}"
 
 
 @pytest.mark.parametrize("M", [65, 4096])
@@ -515,10 +521,17 @@ def test_full_size_post_pre_matches_oracle_on_sampled_rows(attn, ffn):
                                      rng.choice(M, 200, replace=False)]))
     oR1, oR1_bits = o.hc_post(inputs.bits(x)[rows], inputs.bits(R)[rows], post32.numpy()[rows],
                               comb32.numpy()[rows])
-    ref2 = ffn.oracle_pre(oR1_bits)
     ridx = torch.from_numpy(rows).to(gu.DEV)
-    gu.assert_bf16_close(gu.bits_of(Rn[ridx]), oR1, "R' (sampled)")
-    gu.assert_bf16_close(gu.bits_of(y[ridx]), ref2["y"], "y (sampled)")
+    gRn = gu.bits_of(Rn[ridx])
+    gu.assert_bf16_close(gRn, oR1, "R' (sampled)")
+    # the pre half on the GPU's own R' bits of those rows: per-stage bars (coefficients 1e-5)
+    ref2g = ffn.oracle_pre(gRn)
+    gu.assert_bf16_close(gu.bits_of(y[ridx]), ref2g["y"], "y (sampled)")
+    for name, g in (("pre", pre2), ("post", post2), ("comb", comb2)):
+        gu.assert_coef_close(gu.f32_np(g[ridx]), ref2g[name], f"{name} (sampled)")
+    # and against the oracle's whole chain (its own R'), one bf16 rounding of R' apart
+    ref2 = ffn.oracle_pre(oR1_bits)
+    gu.assert_bf16_close(gu.bits_of(y[ridx]), ref2["y"], "y (sampled, oracle chain)")
     for name, g in (("pre", pre2), ("post", post2), ("comb", comb2)):
         err = np.abs(gu.f32_np(g[ridx]) - ref2[name]).max()
-        assert err <= 2e-3, f"{name} (sampled): {err}"
+        assert err <= 2e-3, f"{name} (sampled, oracle chain): {err}"

@@ -78,6 +78,44 @@ def _e4m3_truncating(s):
     return code.astype(np.uint8)
 
 
+_real_pre = o.hc_pre
+_real_head = o.hc_head
+_real_split_sinkhorn = o.hc_split_sinkhorn
+
+
+def _pre_combine_weighted_by_post(R_bits, fn, scale, base, w_bits, rms_eps=1e-6, hc_eps=1e-6,
+                                  iters=20, post_mult=2.0, norm_eps=1e-6):
+    d = _real_pre(R_bits, fn, scale, base, w_bits, rms_eps, hc_eps, iters, post_mult, norm_eps)
+    d["y"], d["y_bits"] = _real_combine_norm(R_bits, d["post"], w_bits, norm_eps)
+    return d
+
+
+def _pre_combine_streams_reversed(R_bits, fn, scale, base, w_bits, rms_eps=1e-6, hc_eps=1e-6,
+                                  iters=20, post_mult=2.0, norm_eps=1e-6):
+    d = _real_pre(R_bits, fn, scale, base, w_bits, rms_eps, hc_eps, iters, post_mult, norm_eps)
+    d["y"], d["y_bits"] = _real_combine_norm(R_bits, d["pre"][:, ::-1], w_bits, norm_eps)
+    return d
+
+
+def _pre_norm_takes_stats_eps(R_bits, fn, scale, base, w_bits, rms_eps=1e-6, hc_eps=1e-6,
+                              iters=20, post_mult=2.0, norm_eps=1e-6):
+    return _real_pre(R_bits, fn, scale, base, w_bits, rms_eps, hc_eps, iters, post_mult, rms_eps)
+
+
+def _head_without_rsqrt(R_bits, fn, scale, base, norm_eps=1e-6, hc_eps=1e-6):
+    R = o.bf16_to_f64(R_bits)
+    mixes = R.reshape(R.shape[0], -1) @ np.asarray(fn, dtype=np.float64).T
+    pre = 1.0 / (1.0 + np.exp(-(mixes * np.asarray(scale).reshape(-1)[0] + base))) + hc_eps
+    y = o.hc_combine(R_bits, pre)
+    return y, o.f64_to_bf16(y)
+
+
+def _split_sinkhorn_without_sinkhorn_eps(mixes, scale, base, hc=4, iters=20, eps=1e-6,
+                                         post_mult=2.0):
+    pre, post, logits = _real_split(mixes, scale, base, hc, eps, post_mult)
+    return pre, post, _real_sinkhorn(logits, iters, 0.0)
+
+
 def _scale_exp_floor(amax):
     amax = np.asarray(amax, dtype=np.float64)
     pos = amax > 0
@@ -101,7 +139,14 @@ def _run_all_pins():
         ("cn_onehot", pins.test_combine_norm_one_hot_pre_is_rms_norm, (3,)),
         ("e4m3_torch", pins.test_e4m3_encode_matches_torch_cast_over_all_bf16_patterns, ()),
         ("mx_minimal", pins.test_mxfp8_scale_exponent_is_minimal_and_safe, ()),
+        ("pre_zero_scale", pins.test_hc_pre_zero_scale_closed_form, ()),
+        ("pre_two_streams", pins.test_hc_pre_two_streams_share_a_column, ()),
+        ("split_sinkhorn_uniform", pins.test_split_sinkhorn_zero_scale_uniform_logits_closed_form, ()),
     ]
+    for i0, h0 in [(0, 0), (2, 5), (3, 7)]:
+        calls.append((f"pre_onehot_{i0}_{h0}", pins.test_hc_pre_one_nonzero_row_closed_form, (i0, h0)))
+    for i0, h0 in [(1, 3), (3, 0)]:
+        calls.append((f"head_onehot_{i0}_{h0}", pins.test_hc_head_one_nonzero_row_closed_form, (i0, h0)))
     for case in pins._golden_sinkhorn():
         calls.append((f"sink_golden_{case[0]}", pins.test_sinkhorn_doubly_stochastic_rownorm_closed_form, (case,)))
     for sh in [(1, 3), (2, 5)]:
@@ -129,6 +174,11 @@ MUTANTS = [
     ("hc_post", _post_comb_transposed, "post_"),
     ("e4m3_encode", _e4m3_truncating, "e4m3_torch"),
     ("mxfp8_scale_exponent", _scale_exp_floor, "mx_"),
+    ("hc_pre", _pre_combine_weighted_by_post, "pre_"),
+    ("hc_pre", _pre_combine_streams_reversed, "pre_"),
+    ("hc_pre", _pre_norm_takes_stats_eps, "pre_"),
+    ("hc_head", _head_without_rsqrt, "head_onehot"),
+    ("hc_split_sinkhorn", _split_sinkhorn_without_sinkhorn_eps, "split_sinkhorn"),
 ]
 
 

@@ -406,8 +406,149 @@ def test_mxfp8_rejects_non_finite():
 
 
 # ------------------------------------------------------------------------------------------
+# hc_pre as a whole: how the stages chain (deepseek_v4.py, DeepseekV4DecoderLayer.hc_pre: the
+# mix stats feed hc_split_sinkhorn, whose pre weights the combine; the norm follows). Each eps
+# gets a distinct value so that a stage reading another stage's eps shows.
+# ------------------------------------------------------------------------------------------
+PRE_RMS_EPS, PRE_HC_EPS, PRE_NORM_EPS = 0.25, 0.01, 0.5
+
+
+def _sig(t: float) -> float:
+    return 1.0 / (1.0 + math.exp(-t))
+
+
+def _pre_params(H, seed):
+    rng = np.random.default_rng(seed)
+    fn = rng.standard_normal((24, 4 * H)) * 0.3
+    scale = np.array([0.7, -0.45, 0.35])
+    base = rng.standard_normal(24)
+    return fn, scale, base
+
+
+def test_split_sinkhorn_zero_scale_uniform_logits_closed_form():
+    """scale = 0 and zero res logits: pre = sigmoid(base) + eps, post = 2 sigmoid(base), and
+    every comb entry is the uniform fixed point (1 - eps) / 4, with one eps for both."""
+    eps = PRE_HC_EPS
+    base = np.concatenate([[0.3, -1.2, 2.0, 0.0], [1.5, -0.5, 0.25, -3.0], np.zeros(16)])
+    mixes = np.random.default_rng(5).standard_normal((3, 24))
+    pre, post, comb = o.hc_split_sinkhorn(mixes, np.zeros(3), base, 4, 20, eps, 2.0)
+    for i in range(4):
+        assert pre[0, i] == pytest.approx(_sig(base[i]) + eps, rel=1e-14)
+        assert post[0, i] == pytest.approx(2.0 * _sig(base[4 + i]), rel=1e-14)
+    np.testing.assert_allclose(comb, (1.0 - eps) / 4.0, rtol=1e-13)
+
+
+def test_hc_pre_zero_scale_closed_form():
+    """scale = 0: pre / post / comb come from base alone, and y is the RMSNorm (norm eps) of
+    the pre-weighted sum of the streams times w; the mixes still carry the stats eps."""
+    H = 8
+    fn, _, base = _pre_params(H, 31)
+    R = inputs.bits(inputs.residual(2, 32, H=H))
+    w = inputs.bits(inputs.norm_weight(33, H=H))
+    d = o.hc_pre(R, fn, np.zeros(3), base, w, rms_eps=PRE_RMS_EPS, hc_eps=PRE_HC_EPS,
+                 norm_eps=PRE_NORM_EPS)
+    xv = o.bf16_to_f64(R)
+    wv = o.bf16_to_f64(w)
+    pre = [_sig(base[i]) + PRE_HC_EPS for i in range(4)]
+    for m in range(2):
+        flat = [xv[m, i, h] for i in range(4) for h in range(H)]
+        r = 1.0 / math.sqrt(sum(v * v for v in flat) / (4 * H) + PRE_RMS_EPS)
+        for f in range(24):
+            assert d["mixes"][m, f] == pytest.approx(sum(fn[f, k] * flat[k] for k in range(4 * H)) * r,
+                                                     rel=1e-12, abs=1e-13)
+        for i in range(4):
+            assert d["pre"][m, i] == pytest.approx(pre[i], rel=1e-14)
+            assert d["post"][m, i] == pytest.approx(2.0 * _sig(base[4 + i]), rel=1e-14)
+        c = [sum(pre[i] * xv[m, i, h] for i in range(4)) for h in range(H)]
+        rn = 1.0 / math.sqrt(sum(v * v for v in c) / H + PRE_NORM_EPS)
+        for h in range(H):
+            assert d["y"][m, h] == pytest.approx(c[h] * rn * wv[h], rel=1e-12, abs=1e-14)
+    np.testing.assert_allclose(d["comb"], o.sinkhorn(np.broadcast_to(base[8:].reshape(4, 4), (2, 4, 4)),
+                                                     20, PRE_HC_EPS), rtol=1e-13)
+
+
+@pytest.mark.parametrize("i0,h0", [(0, 0), (2, 5), (3, 7)])
+def test_hc_pre_one_nonzero_row_closed_form(i0, h0):
+    """One non-zero value v at stream i0, column h0, non-zero scale: mixes = v fn[:, k] /
+    sqrt(v^2 / 4H + rms_eps); y is zero except at h0, where c = pre[i0] v and
+    y = c / sqrt(c^2 / H + norm_eps) * w[h0]."""
+    H = 8
+    fn, scale, base = _pre_params(H, 40 + i0)
+    v = -2.75
+    R = np.zeros((1, 4, H), dtype=np.float64)
+    R[0, i0, h0] = v
+    w = inputs.bits(inputs.norm_weight(41, H=H))
+    wv = o.bf16_to_f64(w)
+    d = o.hc_pre(_bf16_bits_of(R), fn, scale, base, w, rms_eps=PRE_RMS_EPS, hc_eps=PRE_HC_EPS,
+                 norm_eps=PRE_NORM_EPS)
+    k = i0 * H + h0
+    r = 1.0 / math.sqrt(v * v / (4 * H) + PRE_RMS_EPS)
+    mix = [v * fn[f, k] * r for f in range(24)]
+    np.testing.assert_allclose(d["mixes"][0], mix, rtol=1e-13)
+    pre = [_sig(scale[0] * mix[i] + base[i]) + PRE_HC_EPS for i in range(4)]
+    post = [2.0 * _sig(scale[1] * mix[4 + i] + base[4 + i]) for i in range(4)]
+    np.testing.assert_allclose(d["pre"][0], pre, rtol=1e-13)
+    np.testing.assert_allclose(d["post"][0], post, rtol=1e-13)
+    # the combine must be weighted by pre, not post: make sure the two differ here
+    assert abs(pre[i0] - post[i0]) > 0.05
+    logits = np.array([[scale[2] * mix[8 + 4 * i + j] + base[8 + 4 * i + j] for j in range(4)]
+                       for i in range(4)])
+    np.testing.assert_allclose(d["comb"][0], o.sinkhorn(logits[None], 20, PRE_HC_EPS)[0], rtol=1e-13)
+    c = pre[i0] * v
+    want = np.zeros(H)
+    want[h0] = c / math.sqrt(c * c / H + PRE_NORM_EPS) * wv[h0]
+    np.testing.assert_allclose(d["y"][0], want, rtol=1e-13, atol=0)
+
+
+def test_hc_pre_two_streams_share_a_column():
+    """Values v0 (stream 0) and v1 (stream 2) in the same column h: c[h] = pre0 v0 + pre2 v1,
+    so the combine sums over the source streams with their own weights."""
+    H = 4
+    fn, scale, base = _pre_params(H, 50)
+    v0, v1, h = 1.5, -0.625, 2
+    R = np.zeros((1, 4, H))
+    R[0, 0, h], R[0, 2, h] = v0, v1
+    w = np.ones(H)
+    d = o.hc_pre(_bf16_bits_of(R), fn, scale, base, _bf16_bits_of(w), rms_eps=PRE_RMS_EPS,
+                 hc_eps=PRE_HC_EPS, norm_eps=PRE_NORM_EPS)
+    r = 1.0 / math.sqrt((v0 * v0 + v1 * v1) / (4 * H) + PRE_RMS_EPS)
+    mix = [(v0 * fn[f, h] + v1 * fn[f, 2 * H + h]) * r for f in range(24)]
+    pre = [_sig(scale[0] * mix[i] + base[i]) + PRE_HC_EPS for i in range(4)]
+    c = pre[0] * v0 + pre[2] * v1
+    want = np.zeros(H)
+    want[h] = c / math.sqrt(c * c / H + PRE_NORM_EPS)
+    np.testing.assert_allclose(d["y"][0], want, rtol=1e-13, atol=0)
+
+
+# ------------------------------------------------------------------------------------------
 # hc_head
 # ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("i0,h0", [(1, 3), (3, 0)])
+def test_hc_head_one_nonzero_row_closed_form(i0, h0):
+    """deepseek_v4.py, hc_head_torch with a non-zero scale: one value v at (i0, h0) gives
+    mixes[i] = v fn[i, k] / sqrt(v^2 / 4H + norm_eps), pre = sigmoid(mixes * s + b) + hc_eps,
+    and y = pre[i0] v at h0, zero elsewhere (rounded once to bf16)."""
+    H = 8
+    norm_eps, hc_eps = 0.3, 0.02
+    rng = np.random.default_rng(60 + h0)
+    fn = rng.standard_normal((4, 4 * H))
+    base = np.array([0.4, -0.8, 1.1, -0.2])
+    s = 0.9
+    v = 3.25
+    R = np.zeros((1, 4, H))
+    R[0, i0, h0] = v
+    y, yb = o.hc_head(_bf16_bits_of(R), fn, np.array([s]), base, norm_eps, hc_eps)
+    k = i0 * H + h0
+    r = 1.0 / math.sqrt(v * v / (4 * H) + norm_eps)
+    pre = [_sig(v * fn[i, k] * r * s + base[i]) + hc_eps for i in range(4)]
+    want = np.zeros(H)
+    want[h0] = pre[i0] * v
+    np.testing.assert_allclose(y[0], want, rtol=1e-14, atol=0)
+    assert np.array_equal(yb[0], o.f64_to_bf16(want))
+    # the mixes path is live: without the rsqrt scaling the value would differ
+    assert abs(_sig(v * fn[i0, k] * s + base[i0]) - _sig(v * fn[i0, k] * r * s + base[i0])) > 1e-3
+
+
 def test_hc_head_zero_scale_closed_form():
     H = 16
     R = inputs.residual(3, 22, H=H)
