@@ -10,16 +10,21 @@ Infinity Cache.
 
 The default path runs the step as the fused post -> pre (hc_post_pre: one kernel writes R' and
 the FFN site's mix-stat partials in one pass, a second one finishes the pre); --path unfused
-runs hc_post then hc_pre. The metric's timed region has no events inside the steps; the
-dominant kernel (hc_post_pre's first kernel, i.e. hc_post_stats; or hc_post) is timed in a
-second region of the same steps with HIP events around each launch.
+runs hc_post then hc_pre. The metric's timed region has no events inside the steps.
 
-Prints one JSON line: rows/s of the whole step, the HBM roofline of the dominant kernel
-(timed live with HIP events recorded on the stream it runs on, around each launch) and the
-CPU oracle's rows/s on a bounded sample of the same workload. The roofline's "traffic" is the
-HBM byte count that rocprofv3's FETCH_SIZE / WRITE_SIZE counters gave for that kernel; it is
-read from the summary under profiles/ and reported only while the kernel's source files
-still hash to what that summary records (null otherwise).
+Prints one JSON line: rows/s of the whole step, the HBM roofline of the dominant kernel and the
+CPU oracle's rows/s on a bounded sample of the same workload. The dominant kernel (the fused
+path's hc_post_stats, i.e. pipe_kernel<true>; or hc_post) is timed in a region of its own:
+K back-to-back launches on the rotating input sets between one pair of HIP events recorded on
+the stream it runs on, divided by K. The roofline's "traffic" is the HBM byte count that
+rocprofv3's FETCH_SIZE / WRITE_SIZE counters gave for that kernel; it is read from the summary
+under profiles/ and reported only while the kernel's source files still hash to what that
+summary records (null otherwise).
+
+--workload config3 / config4 time the other two chained workloads instead (one JSON line
+each, no CPU baseline): the M = 1500 chain pre(attn) -> post -> pre(ffn), and the M = 16384
+prefill chunk post -> pre(ffn) -> row-local MXFP8 of y (prefill_sp.py, module docstring
+stage 2), run as hc_post_pre_mxfp8.
 """
 from __future__ import annotations
 
@@ -235,6 +240,122 @@ def small_table(args, torch, ops, inputs, d) -> int:
     return 0
 
 
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def back_to_back_ms(torch, fn_, k: int) -> float:
+    """Average time per launch of fn_(i), i = 0 .. k-1, enqueued back to back on torch's
+    current stream between one pair of HIP events recorded on that stream."""
+    e0, e1 = _events(torch)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(k):
+        fn_(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / k
+
+
+def copy_ceiling_gbs(torch, dev) -> float:
+    """A plain 1 GiB device copy (read + write bytes / time): the practical HBM ceiling."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ms = back_to_back_ms(torch, lambda i: dst.copy_(src), 10)
+    del src, dst
+    return 2 * (1 << 30) / (ms * 1e-3) / 1e9
+
+
+# chained workloads other than the metric step, timed with --workload
+CHAIN_WORKLOADS = {
+    # M, rows per op of the chain (survey accounting: each op's algorithmic bytes), sets
+    "config3": dict(M=1500, sets=6,
+                    desc="mHC chain pre(attn) -> post -> pre(ffn), M=1500 rows, H=5120, "
+                         "4 streams: hc_pre then hc_post_pre",
+                    row_bytes=PRE_BYTES_ROW + POST_BYTES_ROW + PRE_BYTES_ROW,
+                    call_bytes=2 * PRE_BYTES_CALL),
+    "config4": dict(M=16384, sets=2,
+                    desc="mHC prefill chunk post -> pre(ffn) -> row-local MXFP8 of y, M=16384 "
+                         "rows, H=5120, 4 streams: hc_post_pre_mxfp8 (R', y bf16, y e4m3 + "
+                         "ue8m0 scales per 32 columns)",
+                    row_bytes=POST_BYTES_ROW + PRE_BYTES_ROW + (2 * H + H + H // 32),
+                    call_bytes=PRE_BYTES_CALL),
+}
+
+
+def chain_workload(args, torch, ops, inputs, d) -> int:
+    wl = CHAIN_WORKLOADS[args.workload]
+    M = wl["M"]
+    dev = torch.device("cuda:0")
+    fn_a, sc_a, ba_a = map(d, inputs.hc_params(inputs.SEED_ATTN))
+    fn_f, sc_f, ba_f = map(d, inputs.hc_params(inputs.SEED_FFN))
+    w_a = d(inputs.norm_weight(inputs.SEED_NORM_ATTN))
+    w_f = d(inputs.norm_weight(inputs.SEED_NORM_FFN))
+    fnp_a, fnp_f = ops.fn_pack(fn_a), ops.fn_pack(fn_f)
+    sets = []
+    for k in range(wl["sets"]):
+        R = d(inputs.residual(M, M + 1000 * k))
+        x = d(inputs.sublayer_out(M, M + 1 + 1000 * k))
+        o = dict(R1=torch.empty_like(R), y=torch.empty(M, H, dtype=torch.bfloat16, device=dev),
+                 y1=torch.empty(M, H, dtype=torch.bfloat16, device=dev),
+                 post=torch.empty(M, HC, device=dev), comb=torch.empty(M, HC, HC, device=dev),
+                 post1=torch.empty(M, HC, device=dev), comb1=torch.empty(M, HC, HC, device=dev),
+                 q=torch.empty(M, H, dtype=torch.uint8, device=dev),
+                 s=torch.empty(M, H // 32, dtype=torch.uint8, device=dev),
+                 ws=torch.empty(ops.post_pre_workspace_bytes(M, H), dtype=torch.uint8, device=dev))
+        # config 4's post takes the attention site's coefficients from a setup pre
+        ops.pre(R, fnp_a, sc_a, ba_a, w_a, out=(o["y1"], o["post1"], o["comb1"], None),
+                workspace=o["ws"])
+        sets.append((R, x, o))
+    torch.cuda.synchronize()
+
+    def step(k):
+        R, x, o = sets[k % len(sets)]
+        if args.workload == "config3":
+            ops.pre(R, fnp_a, sc_a, ba_a, w_a, out=(o["y1"], o["post1"], o["comb1"], None),
+                    workspace=o["ws"])
+            ops.post_pre(x, R, o["post1"], o["comb1"], fnp_f, sc_f, ba_f, w_f,
+                         out=(o["R1"], o["y"], o["post"], o["comb"], None), workspace=o["ws"])
+        else:
+            ops.post_pre_mxfp8(x, R, o["post1"], o["comb1"], fnp_f, sc_f, ba_f, w_f,
+                               R_out=o["R1"],
+                               out=(o["y"], o["q"], o["s"], o["post"], o["comb"], None),
+                               workspace=o["ws"])
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    nbytes = M * wl["row_bytes"] + wl["call_bytes"]
+
+    # the dominant kernel (pipe_kernel<true>, the fused post + mix stats) back to back
+    def post_stats(k):
+        R, x, o = sets[k % len(sets)]
+        ops.post_stats(x, R, o["post1"], o["comb1"], fnp_f, out=o["R1"], workspace=o["ws"])
+    kms = back_to_back_ms(torch, post_stats, args.steps)
+    kbytes = M * POST_BYTES_ROW + FN_BYTES
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "workload": args.workload, "M": M, "H": H, "steps": args.steps, "warmup": args.warmup,
+        "desc": wl["desc"], "ms_per_step": ms, "rows_per_s": M / (ms * 1e-3),
+        "algorithmic_bytes_step": nbytes, "algorithmic_gbps_step": gbs,
+        "algorithmic_frac_step": gbs / PEAK_HBM_GBS,
+        "ideal_us_at_peak": nbytes / (PEAK_HBM_GBS * 1e9) * 1e6,
+        "roofline": {"kernel": "pipe_kernel<true> (hc_post_stats)", "bound": "hbm",
+                     "ms": kms, "achieved": kbytes / (kms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": kbytes / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "algorithmic_bytes": kbytes},
+        "input_sets": len(sets),
+    }), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +372,10 @@ def main() -> int:
     ap.add_argument("--small", action="store_true",
                     help="instead of the step: GPU time per call of small batches "
                          "(M = 1 .. 1024) from HIP graph replays, one JSON line each")
+    ap.add_argument("--workload", choices=["step", "config3", "config4"], default="step",
+                    help="step: the metric (post + pre at M=4096); config3 / config4: the "
+                         "M=1500 pre -> post -> pre chain or the M=16384 post -> pre -> MXFP8 "
+                         "prefill chunk")
     ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
                     help="fused: hc_post_pre (post with the next pre's mix stats in one pass, "
                          "then the pre finish); unfused: hc_post then hc_pre")
@@ -272,6 +397,8 @@ def main() -> int:
     d = lambda t: t.to(dev).contiguous()  # noqa: E731
     if args.small:
         return small_table(args, torch, ops, inputs, d)
+    if args.workload != "step":
+        return chain_workload(args, torch, ops, inputs, d)
 
     fn_a, sc_a, ba_a = map(d, inputs.hc_params(inputs.SEED_ATTN))
     fn_f, sc_f, ba_f = map(d, inputs.hc_params(inputs.SEED_FFN))
@@ -304,23 +431,23 @@ def main() -> int:
             ops.pre(o["R1"], fnp_f, sc_f, ba_f, w_f, out=(o["y"], o["post"], o["comb"], None),
                     workspace=o["ws"])
 
-    def step_timed(k, ev):
-        """The same kernels with HIP events around each (events cost the step time, so this
-        runs in a region of its own): ev[0] -> ev[1] brackets the dominant kernel."""
+    def first_kernel(k):
+        """The dominant kernel alone: hc_post_stats (pipe_kernel<true>) or hc_post."""
         R, x, post, comb, o = sets[k % len(sets)]
-        ev[0].record()
         if args.path == "fused":
-            # hc_post_pre as its two calls (same kernels, same bits)
             ops.post_stats(x, R, post, comb, fnp_f, out=o["R1"], workspace=o["ws"])
-            ev[1].record()
+        else:
+            ops.post(x, R, post, comb, out=o["R1"])
+
+    def second_part(k):
+        """The rest of the step alone, on the R' the first kernel left in the same set."""
+        R, x, post, comb, o = sets[k % len(sets)]
+        if args.path == "fused":
             ops.pre_finish(o["R1"], o["ws"], sc_f, ba_f, w_f,
                            out=(o["y"], o["post"], o["comb"], None))
         else:
-            ops.post(x, R, post, comb, out=o["R1"])
-            ev[1].record()
             ops.pre(o["R1"], fnp_f, sc_f, ba_f, w_f, out=(o["y"], o["post"], o["comb"], None),
                     workspace=o["ws"])
-        ev[2].record()
 
     for k in range(args.warmup):
         step(k)
@@ -335,27 +462,11 @@ def main() -> int:
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
-    # the dominant kernel's region: K more steps with events around each kernel
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        step_timed(k, evs[k])
-    torch.cuda.synchronize()
-    first_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    second_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-
-    # practical HBM ceiling for context: a plain 1 GiB device copy
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(10):
-        dst.copy_(src)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * src.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
+    # the dominant kernel's region: K launches back to back between one event pair; then the
+    # second part of the step the same way (each set's R' and workspace are from its step)
+    first_ms = back_to_back_ms(torch, first_kernel, args.steps)
+    second_ms = back_to_back_ms(torch, second_part, args.steps)
+    copy_gbs = copy_ceiling_gbs(torch, dev)
 
     kname, kbytes, kfiles = ROOFLINE_KERNEL[args.path]
     k_gbs = kbytes / (first_ms * 1e-3) / 1e9
@@ -386,12 +497,15 @@ def main() -> int:
             "M": M, "H": H, "hc": HC, "io_dtype": "bf16", "input_sets": args.sets,
             "parallelism": "none (1 GPU)",
         },
-        "achieved_gbps_step": step_gbs,
-        "hbm_frac_step": step_gbs / PEAK_HBM_GBS,
+        # the step's algorithmic bytes (each op's own inputs and outputs, R' counted as written
+        # by the post and read by the pre) over its wall-clock time; part of the R' read may be
+        # served by the Infinity Cache, so this is not an HBM-only figure
+        "algorithmic_gbps_step": step_gbs,
+        "algorithmic_frac_step": step_gbs / PEAK_HBM_GBS,
         "algorithmic_bytes_step": STEP_BYTES,
         "copy_ceiling_gbps": copy_gbs,
         "path": args.path,
-        "kernels_ms": kernels_ms,
+        "kernels_ms_back_to_back": kernels_ms,
         "roofline": {
             "kernel": kname,
             "bound": "hbm",
