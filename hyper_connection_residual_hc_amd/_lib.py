@@ -40,6 +40,9 @@ SIGNATURES = {
     "hc_post_pre": (_int, [_p, _i64, _p, _i64, _p, _p, _p, _p, _p, _p, _i64, _i32, _f32, _f32,
                            _f32, _i32, _f32, _f32, _p, _i64, _p, _i64, _p, _p, _p, _p, _sz,
                            _p]),
+    "hc_post_pre_noalloc": (_int, [_p, _i64, _p, _i64, _p, _p, _p, _p, _p, _p, _i64, _i32, _f32,
+                                   _f32, _f32, _i32, _f32, _f32, _p, _i64, _p, _i64, _p, _p, _p,
+                                   _p]),
     "hc_post_stats": (_int, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _i32, _p, _i64, _p, _sz, _p]),
     "hc_pre_finish": (_int, [_p, _i64, _p, _p, _p, _i64, _i32, _f32, _f32, _f32, _i32, _f32, _f32,
                              _p, _i64, _p, _p, _p, _p, _sz, _p]),

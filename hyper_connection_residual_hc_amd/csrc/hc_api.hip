@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/hc_mi355x.h"
 #include "hc_launch.h"
 
@@ -523,6 +525,80 @@ HC_API int hc_head(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, co
   if ((st = launched(hc::launch_stats(R, ldR, fn_packed, (int)M, H, part, s)))) return st;
   return launched(hc::launch_head_finish(part, R, ldR, scale, base, (int)M, H, norm_eps, hc_eps,
                                          y, ldY, s));
+}
+
+// ---- hc_post_pre without a caller workspace ----------------------------------------------------
+// The stats partials of up to HC_NOALLOC_MAX_ROWS rows live in a file-scope device array, one
+// copy per GPU for the life of the process. Host code never passes the array's name to a kernel
+// (on the host that name is only a stand-in): its device address is looked up once per device
+// with hipGetSymbolAddress, with that device current, and kept below.
+}  // extern "C"
+
+static constexpr size_t kScratchBytes =
+    (size_t)hc::kSlices * HC_NOALLOC_MAX_ROWS * hc::kPartStride * 4;
+static_assert(kScratchBytes == (size_t)HC_NOALLOC_SCRATCH_BYTES, "header and library disagree");
+
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's scratch array, or NULL (with *err set) when it cannot be had.
+// The stream must belong to the current device: that device's copy is the one its kernels see.
+void* scratch_for(void* stream, int* err) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = HC_ERR_LAUNCH;
+    return nullptr;
+  }
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(as_stream(stream), &sdev) != hipSuccess) {
+      *err = HC_ERR_ARG;
+      return nullptr;
+    }
+    if ((int)sdev != dev) {
+      *err = HC_ERR_ARG;
+      return nullptr;
+    }
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      *err = HC_ERR_LAUNCH;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+HC_API int hc_post_pre_noalloc(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                               const float* post, const float* comb, const uint16_t* fn_packed,
+                               const float* scale, const float* base, const uint16_t* weight,
+                               int64_t M, int32_t H, float rms_eps, float pre_eps,
+                               float sinkhorn_eps, int32_t iters, float post_mult,
+                               float norm_eps, uint16_t* Rout, int64_t ldOut, uint16_t* y,
+                               int64_t ldY, float* pre_out, float* post_out, float* comb_out,
+                               void* stream) {
+  int st = check_m(M);
+  if (st) return st;
+  if (M > HC_NOALLOC_MAX_ROWS) return HC_ERR_WORKSPACE;  // beyond the scratch array
+  void* ws = nullptr;  // an empty call checks its arguments and never touches the array
+  if (M > 0 && !(ws = scratch_for(stream, &st))) return st;
+  const Finish f{scale, base, weight, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult, norm_eps,
+                 y, ldY, nullptr, 0, nullptr, 0, pre_out, post_out, comb_out};
+  return post_pre_impl(x, ldX, R, ldR, post, comb, fn_packed, M, H, Rout, ldOut, f, false, ws,
+                       kScratchBytes, stream);
 }
 
 // ---- 128x4 scale layout ----------------------------------------------------------------------

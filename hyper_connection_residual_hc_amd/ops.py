@@ -304,6 +304,45 @@ def post_pre(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.
     return Rn, y, post_o, comb_o, pre_o
 
 
+NOALLOC_MAX_ROWS = 16384  # HC_NOALLOC_MAX_ROWS
+
+
+def post_pre_noalloc(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.Tensor,
+                     fn_packed: torch.Tensor, scale: torch.Tensor, base: torch.Tensor,
+                     weight: torch.Tensor, out, rms_eps: float = RMS_EPS,
+                     pre_eps: float = HC_EPS, sinkhorn_eps: float = HC_EPS, iters: int = ITERS,
+                     post_mult: float = POST_MULT, norm_eps: float = RMS_EPS):
+    """post_pre with the library's static scratch array instead of a workspace (at most
+    NOALLOC_MAX_ROWS rows; calls on one GPU must not overlap). The caller passes every
+    output: out = (R' [M, 4, H], y [M, H], post' [M, 4], comb' [M, 4, 4], pre' [M, 4] or
+    None); nothing is allocated here either."""
+    M, H, ldR = _residual(R)
+    _need(x, "x", torch.bfloat16, 2)
+    if tuple(x.shape) != (M, H):
+        raise ValueError(f"x must be [{M}, {H}]")
+    _contig(post_, "post", torch.float32, (M, HC))
+    _contig(comb, "comb", torch.float32, (M, HC, HC))
+    _contig(scale, "scale", torch.float32, (3,))
+    _contig(base, "base", torch.float32, (MIX,))
+    _contig(weight, "weight", torch.bfloat16, (H,))
+    Rn, y, post_o, comb_o, pre_o = out
+    _packed(fn_packed, H)
+    _shaped(Rn, "R_out", torch.bfloat16, (M, HC, H))
+    _, _, ldOut = _residual(Rn)
+    _shaped(y, "y", torch.bfloat16, (M, H))
+    _contig(post_o, "post_out", torch.float32, (M, HC))
+    _contig(comb_o, "comb_out", torch.float32, (M, HC, HC))
+    if pre_o is not None:
+        _contig(pre_o, "pre_out", torch.float32, (M, HC))
+    _one_device(x, R, post_, comb, fn_packed, scale, base, weight, Rn, y, post_o, comb_o, pre_o)
+    _lib.call("hc_post_pre_noalloc", x.data_ptr(), _rows(x, H), R.data_ptr(), ldR,
+              post_.data_ptr(), comb.data_ptr(), fn_packed.data_ptr(), scale.data_ptr(),
+              base.data_ptr(), weight.data_ptr(), M, H, rms_eps, pre_eps, sinkhorn_eps, iters,
+              post_mult, norm_eps, Rn.data_ptr(), ldOut, y.data_ptr(), _rows(y, H), _ptr(pre_o),
+              post_o.data_ptr(), comb_o.data_ptr(), _stream(R))
+    return Rn, y, post_o, comb_o, pre_o
+
+
 # ---- the two halves of the fused post -> pre ----------------------------------------------------
 def post_stats(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.Tensor,
                fn_packed: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -199,6 +199,31 @@ HC_API int hc_post_pre(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_
                        size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * hc_post_pre for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. The same kernels and bits as
+ * hc_post_pre; instead of a caller workspace it uses a static device array inside the library
+ * (HC_NOALLOC_SCRATCH_BYTES = 16 MiB, one copy per GPU, held until the process ends). It calls
+ * no allocating routine. The array's device address is looked up on the first call on each
+ * device, so make that first call outside a graph capture.
+ *
+ * Arguments and outputs as hc_post_pre, without workspace / workspace_bytes. M is at most
+ * HC_NOALLOC_MAX_ROWS (16384; larger M returns HC_ERR_WORKSPACE). `stream` must belong to the
+ * current device (HC_ERR_ARG otherwise). Every partial in the array is written before it is
+ * read, so nothing has to start at zero; but all calls on one GPU share the array, so calls
+ * that overlap in time on one GPU (other streams, other threads) race and must not be issued.
+ * ------------------------------------------------------------------------------------- */
+#define HC_NOALLOC_MAX_ROWS 16384
+#define HC_NOALLOC_SCRATCH_BYTES (8 * 16384 * 32 * 4)
+HC_API int hc_post_pre_noalloc(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
+                               const float* post, const float* comb, const uint16_t* fn_packed,
+                               const float* scale, const float* base, const uint16_t* weight,
+                               int64_t M, int32_t H, float rms_eps, float pre_eps,
+                               float sinkhorn_eps, int32_t iters, float post_mult,
+                               float norm_eps, uint16_t* Rout, int64_t ldOut, uint16_t* y,
+                               int64_t ldY, float* pre_out, float* post_out, float* comb_out,
+                               void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * hc_post_pre in two calls, for callers that place other work between the halves or time
  * them apart. hc_post_stats followed by hc_pre_finish on the same stream, with the same
  * workspace, M and H and with hc_pre_finish's R = hc_post_stats's Rout (same pointer and
