@@ -251,7 +251,12 @@ __global__ __launch_bounds__(256) void head_finish_kernel(
 }
 
 // ---- dispatch over the compiled H values ----------------------------------------------------
-#define HC_FOR_EACH_NG(X) X(1) X(2) X(4) X(8) X(10) X(14) X(16)
+// One kernel per row width H = 512 n, n = 1 .. 16 (every multiple of 512 up to 8192). The row
+// lives in registers, so the count of column blocks is a compile-time constant: a runtime count
+// with a compiled maximum was measured at compile time to cost the 5120-wide finish 32 more
+// registers (address registers of the blocks a shorter row skips).
+#define HC_FOR_EACH_NG(X) \
+  X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
 
 bool combine_h_supported(int H) {
   if (H % 512) return false;

@@ -120,7 +120,7 @@ HC_API int hc_sinkhorn(const float* mixes, int64_t M, const float* scale, const 
  *
  * R: bf16 [M, 4, H] (ldR); pre: fp32 [M, 4] with row stride ldPre >= 4 (ldPre*4 bytes,
  * 16-byte aligned); weight: bf16 [H]; y: bf16 [M, H] (ldY >= H), written.
- * H: 512 * n for n in {1, 2, 4, 8, 10, 14, 16}.
+ * H: a multiple of 512 up to 8192 (512 * n, n = 1 .. 16).
  * ------------------------------------------------------------------------------------- */
 HC_API int hc_combine_norm(const uint16_t* R, int64_t ldR, const float* pre, int64_t ldPre,
                            const uint16_t* weight, int64_t M, int32_t H, float eps,

@@ -63,7 +63,8 @@ def test_validation_codes(L):
     assert L.hc_sinkhorn(None, 3, None, None, 20, 1e-6, 1e-6, 2.0, None, None, None, None) == 1
     # shapes
     assert L.hc_post(fake, H, fake, 4 * H, fake, fake, 5, 640, fake, 4 * H, None) == 2
-    assert L.hc_combine_norm(fake, 4 * H, fake, 4, fake, 5, 3 * 512, 1e-6, fake, H, None) == 2
+    assert L.hc_combine_norm(fake, 4 * H, fake, 4, fake, 5, 17 * 512, 1e-6, fake, H, None) == 2  # > 8192
+    assert L.hc_combine_norm(fake, 4 * H, fake, 4, fake, 5, 3 * 256, 1e-6, fake, H, None) == 2  # not 512 n
     assert L.hc_sinkhorn(fake, 3, fake, fake, 0, 1e-6, 1e-6, 2.0, fake, fake, fake, None) == 2
     assert L.mxfp8_quant_rows(fake, 40, 2, 40, fake, 40, fake, 1, None) == 2
     assert L.hc_post(fake, H, fake, 4 * H - 8, fake, fake, 5, H, fake, 4 * H, None) == 2

@@ -76,3 +76,15 @@ def test_head_zero_scale_and_slices(head):
     for lo, hi in [(0, 375), (375, 750), (1, 18), (63, 192), (M - 5, M)]:
         part = ops.head(R[lo:hi], head["fnp"], head["scale_d"], head["base_d"])
         assert torch.equal(part.view(torch.int16), full[lo:hi].view(torch.int16)), (lo, hi)
+
+
+@pytest.mark.parametrize("Hs,M", [(3072, 130), (6144, 70), (1024, 1100)])
+def test_head_other_widths(Hs, M):
+    """Other row widths (6 and 12 column blocks per lane; two stages per slice with the
+    pipelined kernel at 1100 rows) against the oracle."""
+    gu.say(f"hc_head H={Hs} M={M}")
+    fn, scale, base = inputs.hc_head_params(inputs.SEED_HEAD + 1, H=Hs)
+    R = inputs.residual(M, M + 7, H=Hs)
+    y = ops.head(gu.dev(R), ops.head_fn_pack(gu.dev(fn)), gu.dev(scale), gu.dev(base))
+    want, _ = o.hc_head(inputs.bits(R), fn.numpy(), scale.numpy(), base.numpy())
+    gu.assert_bf16_close(gu.bits_of(y), want, "head y")

@@ -353,10 +353,10 @@ def test_binding_rejects_short_outputs(attn, ffn):
         ops.pre_finish_mxfp8(R1, spread[::2], ffn.scale_d, ffn.base_d, ffn.w_d)
 
 
-@pytest.mark.parametrize("Hs", [2048, 7168, 8192])
+@pytest.mark.parametrize("Hs", [2048, 3072, 4096, 6144, 7168, 8192])
 def test_wider_hidden_sizes(Hs):
-    """The other compiled widths (4, 14 and 16 column blocks of 512 per lane; 4, 14 and 16
-    stages per slice): pre and post vs the oracle, the fused op vs post then pre."""
+    """Other row widths (4 to 16 column blocks of 512 per lane; as many stages per slice): pre
+    and post vs the oracle, the fused op vs post then pre."""
     gu.say(f"H={Hs}")
     site = gu.Site(15, 16, H_=Hs)
     nxt = gu.Site(17, 18, H_=Hs)
@@ -376,6 +376,33 @@ def test_wider_hidden_sizes(Hs):
     assert torch.equal(full[0].view(torch.int16), Rn.view(torch.int16))
     assert torch.equal(full[1].view(torch.int16), y2.view(torch.int16))
     assert torch.equal(full[2], post2) and torch.equal(full[3], comb2)
+    oR, oR_bits = o.hc_post(inputs.bits(x.cpu()), inputs.bits(R), gu.f32_np(post), gu.f32_np(comb))
+    gu.assert_bf16_close(gu.bits_of(Rn), oR, "R'")
+    ref2 = nxt.oracle_pre(gu.bits_of(Rn))
+    gu.assert_coef_close(gu.f32_np(comb2), ref2["comb"], "comb (next site)")
+    gu.assert_bf16_close(gu.bits_of(y2), ref2["y"], "y (next site)")
+
+
+@pytest.mark.parametrize("Hs", [512, 1536, 2560, 3584, 4608, 5632, 6656, 7680])
+def test_combine_norm_and_post_at_odd_block_counts(Hs):
+    """Row widths that are odd multiples of 512 (1 to 15 column blocks per lane), which the
+    combine + norm and the post take (the mix stats need a multiple of 1024): both vs the
+    oracle, on rows with a ragged tail of waves."""
+    gu.say(f"combine_norm / post H={Hs}")
+    M = 37
+    R = inputs.residual(M, 30, H=Hs)
+    x = inputs.sublayer_out(M, 31, H=Hs)
+    w = inputs.norm_weight(32, H=Hs)
+    rng = np.random.default_rng(Hs)
+    pre = torch.from_numpy(rng.random((M, 4)).astype(np.float32) + 1e-6)
+    post = torch.from_numpy((2 * rng.random((M, 4))).astype(np.float32))
+    comb = torch.from_numpy(rng.dirichlet(np.ones(4), size=(M, 4)).astype(np.float32))
+    y = ops.combine_norm(gu.dev(R), gu.dev(pre), gu.dev(w))
+    oy, _ = o.hc_combine_norm(inputs.bits(R), pre.numpy(), inputs.bits(w))
+    gu.assert_bf16_close(gu.bits_of(y), oy, "y")
+    Rn = ops.post(gu.dev(x), gu.dev(R), gu.dev(post), gu.dev(comb))
+    oR, _ = o.hc_post(inputs.bits(x), inputs.bits(R), post.numpy(), comb.numpy())
+    gu.assert_bf16_close(gu.bits_of(Rn), oR, "R'")
 
 
 def test_narrowest_hidden_size_two_stages_per_slice():
