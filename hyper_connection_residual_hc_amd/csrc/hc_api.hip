@@ -39,12 +39,16 @@ int launched(hipError_t err) { return err == hipSuccess ? HC_OK : HC_ERR_LAUNCH;
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-bool stats_h_ok(int32_t H) { return H > 0 && H % 1024 == 0 && H <= (1 << 20); }
+bool stats_h_ok(int32_t H) { return hc::stats_geom(H).S > 0; }  // H = 1024 n <= 8192
 bool post_h_ok(int32_t H) { return H > 0 && H % 512 == 0 && H <= (1 << 20); }
+
+// Row strides stay below 2^26 elements (the stats kernels address 16 rows of any array with
+// 32-bit byte offsets).
+constexpr int64_t kMaxLd = (int64_t)1 << 26;
 
 // R [M, 4, H] bf16 with row stride ldR
 int check_residual(const uint16_t* R, int64_t ldR, int32_t H) {
-  if (ldR < (int64_t)kHC * H) return HC_ERR_SHAPE;
+  if (ldR < (int64_t)kHC * H || ldR >= kMaxLd) return HC_ERR_SHAPE;
   if (!al16(R) || (ldR * 2) % 16) return HC_ERR_ALIGN;
   return HC_OK;
 }
@@ -114,14 +118,14 @@ int finish_pointers(const Finish& f, int64_t M, int32_t H, bool mx, Span* ins, S
   return HC_OK;
 }
 
-int workspace_ok(const void* ws, size_t bytes, int64_t M) {
-  if (!ws || bytes < hc::stats_workspace_bytes(M)) return HC_ERR_WORKSPACE;
+int workspace_ok(const void* ws, size_t bytes, int64_t M, int32_t H) {
+  if (!ws || bytes < hc::stats_workspace_bytes(M, H)) return HC_ERR_WORKSPACE;
   if (((uintptr_t)ws & 255u) != 0) return HC_ERR_ALIGN;
   return HC_OK;
 }
 
-Span workspace_span(const void* ws, int64_t M) {
-  return Span{(uintptr_t)ws, (uintptr_t)ws + hc::stats_workspace_bytes(M)};
+Span workspace_span(const void* ws, int64_t M, int32_t H) {
+  return Span{(uintptr_t)ws, (uintptr_t)ws + hc::stats_workspace_bytes(M, H)};
 }
 
 hipError_t launch_finish(const float* part, const uint16_t* R, int64_t ldR, const Finish& f,
@@ -144,10 +148,10 @@ int pre_impl(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, int64_t 
   if ((st = finish_pointers(f, M, H, mx, ins, outs))) return st;
   if ((st = check_residual(R, ldR, H))) return st;
   if (!al16(fn_packed)) return HC_ERR_ALIGN;
-  if ((st = workspace_ok(workspace, workspace_bytes, M))) return st;
+  if ((st = workspace_ok(workspace, workspace_bytes, M, H))) return st;
   ins[3] = rows_span(R, M, ldR, (int64_t)kHC * H, 2);
   ins[4] = Span{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)};
-  outs[6] = workspace_span(workspace, M);
+  outs[6] = workspace_span(workspace, M, H);
   if ((st = no_alias(ins, 5, outs, 7))) return st;
   float* part = static_cast<float*>(workspace);
   hipStream_t s = as_stream(stream);
@@ -166,9 +170,9 @@ int finish_impl(const uint16_t* R, int64_t ldR, int64_t M, int32_t H, const Fini
   Span ins[5], outs[6];
   if ((st = finish_pointers(f, M, H, mx, ins, outs))) return st;
   if ((st = check_residual(R, ldR, H))) return st;
-  if ((st = workspace_ok(workspace, workspace_bytes, M))) return st;
+  if ((st = workspace_ok(workspace, workspace_bytes, M, H))) return st;
   ins[3] = rows_span(R, M, ldR, (int64_t)kHC * H, 2);
-  ins[4] = workspace_span(workspace, M);
+  ins[4] = workspace_span(workspace, M, H);
   if ((st = no_alias(ins, 5, outs, 6))) return st;
   return launched(launch_finish(static_cast<const float*>(workspace), R, ldR, f, M, H, mx,
                                 as_stream(stream)));
@@ -182,18 +186,18 @@ int post_stats_check(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t 
   int st;
   if (!x || !R || !post || !comb || !fn_packed || !Rout) return HC_ERR_NULL;
   if ((st = check_residual(R, ldR, H))) return st;
-  if (ldX < H || ldOut < (int64_t)kHC * H) return HC_ERR_SHAPE;
+  if (ldX < H || ldOut < (int64_t)kHC * H || ldX >= kMaxLd || ldOut >= kMaxLd) return HC_ERR_SHAPE;
   if (!al16(x) || !al16(Rout) || !al16(post) || !al16(comb) || !al16(fn_packed) ||
       (ldX * 2) % 16 || (ldOut * 2) % 16)
     return HC_ERR_ALIGN;
-  if ((st = workspace_ok(workspace, workspace_bytes, M))) return st;
+  if ((st = workspace_ok(workspace, workspace_bytes, M, H))) return st;
   ins[0] = rows_span(x, M, ldX, H, 2);
   ins[1] = rows_span(R, M, ldR, (int64_t)kHC * H, 2);
   ins[2] = rows_span(post, M, kHC, kHC, 4);
   ins[3] = rows_span(comb, M, kHC * kHC, kHC * kHC, 4);
   ins[4] = Span{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)};
   outs[0] = rows_span(Rout, M, ldOut, (int64_t)kHC * H, 2);
-  outs[1] = workspace_span(workspace, M);
+  outs[1] = workspace_span(workspace, M, H);
   return HC_OK;
 }
 
@@ -270,7 +274,7 @@ HC_API int hc_head_fn_pack(const float* fn, int32_t H, uint16_t* fn_packed, void
 // ---- stage 1 -----------------------------------------------------------------------------
 HC_API size_t hc_pre_stats_workspace_bytes(int64_t M, int32_t H) {
   if (M < 0 || !stats_h_ok(H)) return 0;
-  return hc::stats_workspace_bytes(M);
+  return hc::stats_workspace_bytes(M, H);
 }
 
 HC_API int hc_pre_stats(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, int64_t M,
@@ -284,12 +288,12 @@ HC_API int hc_pre_stats(const uint16_t* R, int64_t ldR, const uint16_t* fn_packe
   if (!R || !fn_packed || !mixes) return HC_ERR_NULL;
   if ((st = check_residual(R, ldR, H))) return st;
   if (!al16(fn_packed)) return HC_ERR_ALIGN;
-  if (!workspace || workspace_bytes < hc::stats_workspace_bytes(M)) return HC_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < hc::stats_workspace_bytes(M, H)) return HC_ERR_WORKSPACE;
   if (((uintptr_t)workspace & 255u) != 0) return HC_ERR_ALIGN;
   const Span r = rows_span(R, M, ldR, (int64_t)kHC * H, 2);
   const Span fp{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)};
   const Span mx = rows_span(mixes, M, kMix, kMix, 4);
-  const Span ws{(uintptr_t)workspace, (uintptr_t)workspace + hc::stats_workspace_bytes(M)};
+  const Span ws{(uintptr_t)workspace, (uintptr_t)workspace + hc::stats_workspace_bytes(M, H)};
   if (overlaps(mx, r) || overlaps(mx, fp) || overlaps(ws, r) || overlaps(ws, fp) ||
       overlaps(ws, mx))
     return HC_ERR_ALIAS;
@@ -513,12 +517,12 @@ HC_API int hc_head(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, co
   if ((st = check_residual(R, ldR, H))) return st;
   if (ldY < H) return HC_ERR_SHAPE;
   if (!al16(fn_packed) || !al16(y) || (ldY * 2) % 16) return HC_ERR_ALIGN;
-  if ((st = workspace_ok(workspace, workspace_bytes, M))) return st;
+  if ((st = workspace_ok(workspace, workspace_bytes, M, H))) return st;
   const Span ins[4] = {rows_span(R, M, ldR, (int64_t)kHC * H, 2),
                        Span{(uintptr_t)fn_packed, (uintptr_t)fn_packed + hc_fn_packed_bytes(H)},
                        Span{(uintptr_t)scale, (uintptr_t)scale + 4},
                        Span{(uintptr_t)base, (uintptr_t)base + kHC * 4}};
-  const Span outs[2] = {rows_span(y, M, ldY, H, 2), workspace_span(workspace, M)};
+  const Span outs[2] = {rows_span(y, M, ldY, H, 2), workspace_span(workspace, M, H)};
   if ((st = no_alias(ins, 4, outs, 2))) return st;
   float* part = static_cast<float*>(workspace);
   hipStream_t s = as_stream(stream);
@@ -528,15 +532,14 @@ HC_API int hc_head(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, co
 }
 
 // ---- hc_post_pre without a caller workspace ----------------------------------------------------
-// The stats partials of up to HC_NOALLOC_MAX_ROWS rows live in a file-scope device array, one
-// copy per GPU for the life of the process. Host code never passes the array's name to a kernel
-// (on the host that name is only a stand-in): its device address is looked up once per device
-// with hipGetSymbolAddress, with that device current, and kept below.
+// The stats partials live in a file-scope device array of HC_NOALLOC_SCRATCH_BYTES, one copy per
+// GPU for the life of the process. Host code never passes the array's name to a kernel (on the
+// host that name is only a stand-in): its device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept below.
 }  // extern "C"
 
-static constexpr size_t kScratchBytes =
-    (size_t)hc::kSlices * HC_NOALLOC_MAX_ROWS * hc::kPartStride * 4;
-static_assert(kScratchBytes == (size_t)HC_NOALLOC_SCRATCH_BYTES, "header and library disagree");
+static constexpr size_t kScratchBytes = (size_t)HC_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
 
 static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
 
@@ -592,7 +595,8 @@ HC_API int hc_post_pre_noalloc(const uint16_t* x, int64_t ldX, const uint16_t* R
                                void* stream) {
   int st = check_m(M);
   if (st) return st;
-  if (M > HC_NOALLOC_MAX_ROWS) return HC_ERR_WORKSPACE;  // beyond the scratch array
+  if (stats_h_ok(H) && hc::stats_workspace_bytes(M, H) > kScratchBytes)
+    return HC_ERR_WORKSPACE;  // more rows than the scratch array holds at this H
   void* ws = nullptr;  // an empty call checks its arguments and never touches the array
   if (M > 0 && !(ws = scratch_for(stream, &st))) return st;
   const Finish f{scale, base, weight, rms_eps, pre_eps, sinkhorn_eps, iters, post_mult, norm_eps,

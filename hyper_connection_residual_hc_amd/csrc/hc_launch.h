@@ -9,35 +9,86 @@
 
 namespace hc {
 
-// Stats split-K geometry: 8 column slices (slice s = columns [s*H/8, (s+1)*H/8) of every
-// stream; block b takes slice b % 8, so each XCD keeps one slice's fn in its L2);
-// 32-column chunks inside a slice; 5 B-operand tiles of 16 packed columns (hi | mid | lo
-// parts of the 24 fn rows, padded to 80).
-constexpr int kSlices = 8;
-constexpr int kPackTiles = 5;
-constexpr int kStatsRows = 64;        // rows per stats tile
-constexpr int kPartStride = 32;       // floats per (slice, row) partial record: 24 dots + sumsq
-__host__ __device__ inline int64_t chunks_per_slice(int H) { return (int64_t)4 * (H / kSlices) / 32; }
-inline int64_t packed_fn_elems(int H) { return (int64_t)kSlices * chunks_per_slice(H) * kPackTiles * 64 * 8; }
-inline size_t stats_workspace_bytes(int64_t M) { return (size_t)kSlices * (size_t)M * kPartStride * 4; }
+// Stats split-K geometry. The 4H columns of a flattened row split into S column slices: slice s
+// covers columns [s W, (s + 1) W) of every stream, W = H / S = 32 NC (NC MFMA chunks of 32
+// columns per stream). NC is the largest even value up to 10 with S = H / (32 NC) a multiple of
+// 4 and at least 8: a stats block keeps its slice's whole packed fn (NC chunks x 5 B-operand
+// tiles per stream, 20 NC registers per lane) in the registers of four MFMA waves, so the slice
+// must stay narrow; the stats kernels need H a multiple of 1024 and at most 8192.
+//   H:  1024 2048 3072 4096 5120 6144 7168 8192
+//   NC:    4    8    8    8   10    8    8    8
+//   S:     8    8   12   16   16   24   28   32
+// Each (slice, row) gets a partial record of kPartStride floats: the 24 partial dots of that
+// slice's columns and their partial sum of squares.
+constexpr int kPackTiles = 5;         // B-operand tiles of 16 packed (part, fn row) columns
+constexpr int kGroupRows = 16;        // rows of one MFMA row tile (a stats row group)
+constexpr int kPartStride = 25;       // floats per (slice, row) partial record: 24 dots + sumsq
+constexpr int kMaxStatsH = 8192;
 
-// Sum of one field of a row's slice partials, in slice order. Used by every consumer
-// of the partials, so the standalone and the fused pre give identical bits.
-__device__ __forceinline__ float slice_sum(const float (&v)[kSlices]) {
-  float t = 0.0f;
+struct StatsGeom {
+  int S;   // column slices
+  int NC;  // 32-column MFMA chunks of each stream in a slice
+  int W;   // slice width (columns of each stream)
+};
+__host__ __device__ inline StatsGeom stats_geom(int H) {
+  StatsGeom g{0, 0, 0};
+  if (H <= 0 || H % 1024 || H > kMaxStatsH) return g;
+  for (int nc = 10; nc >= 2; nc -= 2) {
+    if (H % (32 * nc)) continue;
+    const int S = H / (32 * nc);
+    if (S % 4 || S < 8) continue;
+    g.S = S;
+    g.NC = nc;
+    g.W = 32 * nc;
+    return g;
+  }
+  return g;
+}
+inline int64_t packed_fn_elems(int H) { return (int64_t)4 * H * kPackTiles * 16; }
+inline size_t stats_workspace_bytes(int64_t M, int H) {
+  return (size_t)stats_geom(H).S * (size_t)M * kPartStride * 4;
+}
+
+// Sum over the S slices of one field of a row's partial records, in the one order every
+// consumer of the partials uses: four interleaved running sums t_g = p[g] + p[g + 4] + ...
+// (g = 0..3, slices in increasing order), then (t_0 + t_1) + (t_2 + t_3). S is a multiple of 4,
+// at most kMaxSlices. Every value is loaded before the first add (addresses clamped to the last
+// slice, extra values unused), so the loads overlap.
+constexpr int kMaxSlices = 32;
+constexpr int kMaxSliceRounds = kMaxSlices / 4;
+__device__ __forceinline__ const float* part_at(const float* part, int M, int s, int m, int f) {
+  return part + ((int64_t)s * M + m) * kPartStride + f;
+}
+// t_g of slice group g (the running sum over slices g, g + 4, ... < S)
+__device__ __forceinline__ void slice_group_load(const float* __restrict__ part, int S, int M,
+                                                 int m, int f, int g,
+                                                 float (&v)[kMaxSliceRounds]) {
 #pragma unroll
-  for (int s = 0; s < kSlices; ++s) t += v[s];
+  for (int j = 0; j < kMaxSliceRounds; ++j) v[j] = *part_at(part, M, min(4 * j + g, S - 1), m, f);
+}
+__device__ __forceinline__ float slice_group_sum(const float (&v)[kMaxSliceRounds], int S, int g) {
+  float t = v[0];
+#pragma unroll
+  for (int j = 1; j < kMaxSliceRounds; ++j)
+    if (4 * j + g < S) t += v[j];
   return t;
 }
-__device__ __forceinline__ void slice_load(const float* __restrict__ part, int M, int m, int f,
-                                           float (&v)[kSlices]) {
+__device__ __forceinline__ float slice_sum(const float* __restrict__ part, int S, int M, int m,
+                                           int f) {
+  float v[4][kMaxSliceRounds];
 #pragma unroll
-  for (int s = 0; s < kSlices; ++s) v[s] = part[((int64_t)s * M + m) * kPartStride + f];
+  for (int g = 0; g < 4; ++g) slice_group_load(part, S, M, m, f, g, v[g]);
+  float t[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) t[g] = slice_group_sum(v[g], S, g);
+  return (t[0] + t[1]) + (t[2] + t[3]);
 }
-__device__ __forceinline__ float slice_sum(const float* __restrict__ part, int M, int m, int f) {
-  float v[kSlices];
-  slice_load(part, M, m, f, v);
-  return slice_sum(v);
+// The same sum spread over a wavefront: the lanes of 16-lane group g = lane / 16 hold t_g; two
+// butterfly exchanges across the groups give every lane (t_0 + t_1) + (t_2 + t_3) (each add sees
+// the same two operands in every lane, in one order or the other, so all lanes agree bit for bit).
+__device__ __forceinline__ float slice_group_combine(float t) {
+  t = t + __shfl_xor(t, 16, 64);
+  return t + __shfl_xor(t, 32, 64);
 }
 
 // fn [rows, 4H] (rows <= 24) into the packed stats operands; missing rows are zero

@@ -158,21 +158,21 @@ template <int NG, bool kMx>
 __global__ __launch_bounds__(256) void pre_finish_kernel(
     const float* __restrict__ part, const uint16_t* __restrict__ R, int64_t ldR,
     const float* __restrict__ scale, const float* __restrict__ base,
-    const uint16_t* __restrict__ w, int M, float kf, float rms_eps, float pre_eps, float sk_eps,
+    const uint16_t* __restrict__ w, int M, int S, float kf, float rms_eps, float pre_eps, float sk_eps,
     int iters, float post_mult, float norm_eps, uint16_t* __restrict__ y, int64_t ldY,
     uint8_t* __restrict__ q, int64_t ldQ, uint8_t* __restrict__ sc, int64_t ldS,
     float* __restrict__ pre, float* __restrict__ post, float* __restrict__ comb) {
   const int lane = threadIdx.x & 63;
   const int m = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
   if (m >= M) return;  // wave-uniform: the whole wave leaves together
-  const int e = lane & 15;
-  // Loads in issue order: this lane's slice partials, then the row. Vector loads complete in
-  // order, so the split + Sinkhorn waits only for the partials and runs while the row is in
-  // flight.
-  float pa[kSlices], pc[kSlices], pq[kSlices];
-  slice_load(part, M, m, e & 7, pa);
-  slice_load(part, M, m, 8 + e, pc);
-  slice_load(part, M, m, kMix, pq);
+  const int e = lane & 15, sg = lane >> 4;
+  // Loads in issue order: this lane's slice partials (its 16-lane group's quarter of the
+  // slices), then the row. Vector loads complete in order, so the split + Sinkhorn waits only
+  // for the partials and runs while the row is in flight.
+  float pa[kMaxSliceRounds], pc[kMaxSliceRounds], pq[kMaxSliceRounds];
+  slice_group_load(part, S, M, m, e & 7, sg, pa);
+  slice_group_load(part, S, M, m, 8 + e, sg, pc);
+  slice_group_load(part, S, M, m, kMix, sg, pq);
   const float base_a = base[e & 7];
   const float base_c = base[8 + e];
   __builtin_amdgcn_sched_barrier(0);
@@ -181,11 +181,11 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(
   __builtin_amdgcn_sched_barrier(0);
 
   // mixes for this lane's entries, reduced over the slices exactly as stats_reduce does
-  const float rs = mix_rscale(slice_sum(pq), kf, rms_eps);
+  const float rs = mix_rscale(slice_group_combine(slice_group_sum(pq, S, sg)), kf, rms_eps);
   // lanes e >= 8 carry a copy of lane e - 8's pre/post input; their pre/post value is unused
   // (no branch here, so the loads above stay ahead of the row's)
-  const float mix_a = slice_sum(pa) * rs;
-  const float mix_c = slice_sum(pc) * rs;
+  const float mix_a = slice_group_combine(slice_group_sum(pa, S, sg)) * rs;
+  const float mix_c = slice_group_combine(slice_group_sum(pc, S, sg)) * rs;
   const SplitParams sp{scale[0], scale[1], scale[2], iters, pre_eps, sk_eps, post_mult};
   float pp;
   const float cv = split_sinkhorn_lane(e, mix_a, mix_c, base_a, base_c, sp, &pp);
@@ -213,25 +213,27 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(
 template <int NG>
 __global__ __launch_bounds__(256) void head_finish_kernel(
     const float* __restrict__ part, const uint16_t* __restrict__ R, int64_t ldR,
-    const float* __restrict__ scale, const float* __restrict__ base, int M, float kf,
+    const float* __restrict__ scale, const float* __restrict__ base, int M, int S, float kf,
     float norm_eps, float hc_eps, uint16_t* __restrict__ y, int64_t ldY) {
   constexpr int H = NG * 512;
   const int lane = threadIdx.x & 63;
   const int m = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
   if (m >= M) return;
-  float pd[kHC][kSlices], pq[kSlices];
+  const int sg = lane >> 4;
+  float pd[kHC][kMaxSliceRounds], pq[kMaxSliceRounds];
 #pragma unroll
-  for (int i = 0; i < kHC; ++i) slice_load(part, M, m, i, pd[i]);
-  slice_load(part, M, m, kMix, pq);
+  for (int i = 0; i < kHC; ++i) slice_group_load(part, S, M, m, i, sg, pd[i]);
+  slice_group_load(part, S, M, m, kMix, sg, pq);
   __builtin_amdgcn_sched_barrier(0);
   RowTile<NG> t;
   load_row<NG, false>(R + (int64_t)m * ldR, nullptr, lane, t);
   __builtin_amdgcn_sched_barrier(0);
-  const float rs = mix_rscale(slice_sum(pq), kf, norm_eps);
+  const float rs = mix_rscale(slice_group_combine(slice_group_sum(pq, S, sg)), kf, norm_eps);
   const float s0 = scale[0];
   float p[kHC];
 #pragma unroll
-  for (int i = 0; i < kHC; ++i) p[i] = sigmoidf_(__fmaf_rn(slice_sum(pd[i]) * rs, s0, base[i])) + hc_eps;
+  for (int i = 0; i < kHC; ++i)
+    p[i] = sigmoidf_(__fmaf_rn(slice_group_combine(slice_group_sum(pd[i], S, sg)) * rs, s0, base[i])) + hc_eps;
   uint16_t* yr = y + (int64_t)m * ldY;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
@@ -293,17 +295,19 @@ hipError_t launch_pre_finish(const float* part, const uint16_t* R, int64_t ldR,
                              float* post, float* comb, hipStream_t s) {
   const dim3 grid((unsigned)((M + 3) / 4)), block(256);
   const float kf = (float)(4 * H);
+  const int S = stats_geom(H).S;
+  if (S == 0) return hipErrorInvalidValue;
   switch (H / 512) {
 #define HC_CASE(n)                                                                              \
   case n:                                                                                       \
     if (q)                                                                                      \
       hipLaunchKernelGGL((pre_finish_kernel<n, true>), grid, block, 0, s, part, R, ldR, scale,  \
-                         base, w, M, kf, rms_eps, pre_eps, sk_eps, iters, post_mult, norm_eps,  \
-                         y, ldY, q, ldQ, sc, ldS, pre, post, comb);                             \
+                         base, w, M, S, kf, rms_eps, pre_eps, sk_eps, iters, post_mult,         \
+                         norm_eps, y, ldY, q, ldQ, sc, ldS, pre, post, comb);                   \
     else                                                                                        \
       hipLaunchKernelGGL((pre_finish_kernel<n, false>), grid, block, 0, s, part, R, ldR, scale, \
-                         base, w, M, kf, rms_eps, pre_eps, sk_eps, iters, post_mult, norm_eps,  \
-                         y, ldY, q, ldQ, sc, ldS, pre, post, comb);                             \
+                         base, w, M, S, kf, rms_eps, pre_eps, sk_eps, iters, post_mult,         \
+                         norm_eps, y, ldY, q, ldQ, sc, ldS, pre, post, comb);                   \
     break;
     HC_FOR_EACH_NG(HC_CASE)
 #undef HC_CASE
@@ -318,11 +322,13 @@ hipError_t launch_head_finish(const float* part, const uint16_t* R, int64_t ldR,
                               hipStream_t s) {
   const dim3 grid((unsigned)((M + 3) / 4)), block(256);
   const float kf = (float)(4 * H);
+  const int S = stats_geom(H).S;
+  if (S == 0) return hipErrorInvalidValue;
   switch (H / 512) {
 #define HC_CASE(n)                                                                              \
   case n:                                                                                       \
     hipLaunchKernelGGL(head_finish_kernel<n>, grid, block, 0, s, part, R, ldR, scale, base, M,  \
-                       kf, norm_eps, hc_eps, y, ldY);                                           \
+                       S, kf, norm_eps, hc_eps, y, ldY);                                        \
     break;
     HC_FOR_EACH_NG(HC_CASE)
 #undef HC_CASE

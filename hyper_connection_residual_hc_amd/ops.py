@@ -304,7 +304,12 @@ def post_pre(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.
     return Rn, y, post_o, comb_o, pre_o
 
 
-NOALLOC_MAX_ROWS = 16384  # HC_NOALLOC_MAX_ROWS
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # HC_NOALLOC_SCRATCH_BYTES
+
+
+def noalloc_max_rows(H: int) -> int:
+    """Most rows post_pre_noalloc takes at row width H (its partials must fit the scratch)."""
+    return NOALLOC_SCRATCH_BYTES // post_pre_workspace_bytes(1, H)
 
 
 def post_pre_noalloc(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb: torch.Tensor,
@@ -313,7 +318,7 @@ def post_pre_noalloc(x: torch.Tensor, R: torch.Tensor, post_: torch.Tensor, comb
                      pre_eps: float = HC_EPS, sinkhorn_eps: float = HC_EPS, iters: int = ITERS,
                      post_mult: float = POST_MULT, norm_eps: float = RMS_EPS):
     """post_pre with the library's static scratch array instead of a workspace (at most
-    NOALLOC_MAX_ROWS rows; calls on one GPU must not overlap). The caller passes every
+    noalloc_max_rows(H) rows; calls on one GPU must not overlap). The caller passes every
     output: out = (R' [M, 4, H], y [M, H], post' [M, 4], comb' [M, 4, 4], pre' [M, 4] or
     None); nothing is allocated here either."""
     M, H, ldR = _residual(R)

@@ -202,18 +202,19 @@ HC_API int hc_post_pre(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_
  * hc_post_pre for callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc. The same kernels and bits as
  * hc_post_pre; instead of a caller workspace it uses a static device array inside the library
- * (HC_NOALLOC_SCRATCH_BYTES = 16 MiB, one copy per GPU, held until the process ends). It calls
+ * (HC_NOALLOC_SCRATCH_BYTES = 32 MiB, one copy per GPU, held until the process ends). It calls
  * no allocating routine. The array's device address is looked up on the first call on each
  * device, so make that first call outside a graph capture.
  *
- * Arguments and outputs as hc_post_pre, without workspace / workspace_bytes. M is at most
- * HC_NOALLOC_MAX_ROWS (16384; larger M returns HC_ERR_WORKSPACE). `stream` must belong to the
- * current device (HC_ERR_ARG otherwise). Every partial in the array is written before it is
- * read, so nothing has to start at zero; but all calls on one GPU share the array, so calls
- * that overlap in time on one GPU (other streams, other threads) race and must not be issued.
+ * Arguments and outputs as hc_post_pre, without workspace / workspace_bytes. The call must fit
+ * the array: hc_post_pre_workspace_bytes(M, H) <= HC_NOALLOC_SCRATCH_BYTES (20 971 rows at
+ * H = 5120, 11 983 at 7168, 10 485 at 8192); larger calls return HC_ERR_WORKSPACE. `stream`
+ * must belong to the current device (HC_ERR_ARG otherwise). Every partial in the array is
+ * written before it is read, so nothing has to start at zero; but all calls on one GPU share
+ * the array, so calls that overlap in time on one GPU (other streams, other threads) race and
+ * must not be issued.
  * ------------------------------------------------------------------------------------- */
-#define HC_NOALLOC_MAX_ROWS 16384
-#define HC_NOALLOC_SCRATCH_BYTES (8 * 16384 * 32 * 4)
+#define HC_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
 HC_API int hc_post_pre_noalloc(const uint16_t* x, int64_t ldX, const uint16_t* R, int64_t ldR,
                                const float* post, const float* comb, const uint16_t* fn_packed,
                                const float* scale, const float* base, const uint16_t* weight,

@@ -74,3 +74,26 @@ class Site:
     def oracle_pre(self, R_bits):
         return o.hc_pre(R_bits, self.fn.numpy(), self.scale.numpy(), self.base.numpy(),
                         inputs.bits(self.w))
+
+
+def stats_geom(H):
+    """(slices S, 32-column chunks per stream per slice NC) of the stats kernels at width H, as
+    the packed layout documents it: the largest even NC <= 10 with S = H / 32 NC a multiple of
+    4 and at least 8."""
+    for nc in (10, 8, 6, 4, 2):
+        if H % (32 * nc) == 0 and (H // (32 * nc)) % 4 == 0 and H // (32 * nc) >= 8:
+            return H // (32 * nc), nc
+    raise ValueError(H)
+
+
+def packed_columns(H):
+    """Flattened fn column of every packed element, as an array shaped like the packed layout
+    [slice][stream][chunk][tile][k-group g][lane column n][8] (without the tile and n axes)."""
+    S, NC = stats_geom(H)
+    W = H // S
+    s = np.arange(S)[:, None, None, None, None]
+    q = np.arange(4)[None, :, None, None, None]
+    c = np.arange(NC)[None, None, :, None, None]
+    g = np.arange(4)[None, None, None, :, None]
+    e = np.arange(8)[None, None, None, None, :]
+    return (q * H + s * W + 32 * c + 8 * g + e), S, NC

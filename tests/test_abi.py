@@ -46,7 +46,10 @@ def test_sizes(L):
     assert L.hc_fn_packed_bytes(H) == 8 * (4 * (H // 8) // 32) * 5 * 64 * 8 * 2
     assert L.hc_fn_packed_bytes(512) == 0  # stats need a multiple of 1024
     assert L.hc_fn_packed_bytes(100) == 0
-    assert L.hc_pre_stats_workspace_bytes(4096, H) == 8 * 4096 * 32 * 4
+    # partial records: 16 slices x 25 floats per row at H = 5120; 28 slices at 7168
+    assert L.hc_pre_stats_workspace_bytes(4096, H) == 16 * 4096 * 25 * 4
+    assert L.hc_pre_stats_workspace_bytes(10, 7168) == 28 * 10 * 25 * 4
+    assert L.hc_pre_stats_workspace_bytes(10, 9216) == 0  # the stats stop at 8192
     assert L.hc_pre_workspace_bytes(0, H) == 0
     assert L.hc_pre_stats_workspace_bytes(-1, H) == 0
 
@@ -88,7 +91,7 @@ def test_validation_codes_of_the_post_pre_halves(L):
     a, b, c, d = (ctypes.c_void_p(v) for v in (0x1000000, 0x2000000, 0x3000000, 0x4000000))
     ws = ctypes.c_void_p(0x5000000)
     need = L.hc_post_pre_workspace_bytes(7, H)
-    assert need == 8 * 7 * 32 * 4
+    assert need == 16 * 7 * 25 * 4  # 16 slices x 25 floats per row at H = 5120
     # M = 0 no-ops
     assert L.hc_post_stats(None, 0, None, 0, None, None, None, 0, H, None, 0, None, 0, None) == 0
     assert L.hc_pre_finish(None, 0, None, None, None, 0, H, 1e-6, 1e-6, 1e-6, 20, 2.0, 1e-6,

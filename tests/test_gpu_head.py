@@ -27,22 +27,19 @@ def test_head_fn_pack_holds_four_rows(head):
     """Rows 0..3 of the packed layout reconstruct the head fn (hi + mid + lo); every other
     (row, part) slot is zero."""
     p = o.bf16_to_f64(head["fnp"].cpu().numpy().view(np.uint16))
-    S, NCS = 8, 4 * (gu.H // 8) // 32
-    p = p.reshape(S, NCS, 5, 4, 16, 8)  # s, c, t, g, n, e
+    k_idx, S, NC = gu.packed_columns(gu.H)
+    k_idx = k_idx.reshape(-1)
+    p = p.reshape(S, 4, NC, 5, 4, 16, 8)  # s, q, c, t, g, n, e
     fn = head["fn"].numpy().astype(np.float64)
-    c = np.arange(NCS)
-    col0 = ((c % 8) // 2) * gu.H + 64 * (c // 8) + 32 * (c % 2)
-    k_idx = (np.arange(S)[:, None, None, None] * (gu.H // S) + col0[None, :, None, None]
-             + 8 * np.arange(4)[None, None, :, None] + np.arange(8)[None, None, None, :]).reshape(-1)
     recon = np.zeros_like(fn)
     for t in range(3):  # tiles 0..2 hold part t of fn rows 0..15 in lane column n
         for n in range(16):
-            blk = p[:, :, t, :, n, :].reshape(-1)
+            blk = p[:, :, :, t, :, n, :].reshape(-1)
             if n < 4:
                 recon[n, k_idx] += blk
             else:
                 assert not blk.any()
-    assert not p[:, :, 3:].any()  # rows 16..23 and the padding
+    assert not p[:, :, :, 3:].any()  # rows 16..23 and the padding
     np.testing.assert_allclose(recon, fn, rtol=2.0**-22, atol=0)
 
 

@@ -41,30 +41,22 @@ def test_fn_pack_reconstructs_fn(attn):
     appears exactly once, the padding is zero, and the parts decrease in magnitude."""
     gu.say("fn_pack H=5120 seed=11")
     p = o.bf16_to_f64(attn.fnp.cpu().numpy().view(np.uint16))
-    S = 8  # column slices
-    NCS = 4 * (gu.H // S) // 32  # 32-column chunks per slice
-    p = p.reshape(S, NCS, 5, 4, 16, 8)  # s, c, t, g, n, e
+    k_idx, S, NC = gu.packed_columns(gu.H)
+    p = p.reshape(S, 4, NC, 5, 4, 16, 8)  # s, q, c, t, g, n, e
+    assert (S, NC) == (16, 10)
     fn = attn.fn.numpy().astype(np.float64)
     parts = np.zeros((3,) + fn.shape)
-    # chunk c of slice s: stage c // 8, stream (c % 8) // 2, half c % 2 -> columns
-    # stream*H + s*H/8 + 64*stage + 32*half + 8g + e
-    c = np.arange(NCS)
-    col0 = ((c % 8) // 2) * gu.H + 64 * (c // 8) + 32 * (c % 2)
-    k_idx = (np.arange(S)[:, None, None, None] * (gu.H // S)
-             + col0[None, :, None, None]
-             + 8 * np.arange(4)[None, None, :, None]
-             + np.arange(8)[None, None, None, :]).reshape(-1)
     seen = set()
     for t in range(5):
         for n in range(16):
             f, part = _pack_slot(t, n)
-            blk = p[:, :, t, :, n, :]  # s, c, g, e
+            blk = p[:, :, :, t, :, n, :]  # s, q, c, g, e
             if f < 0:
                 assert np.all(blk == 0)
                 continue
             assert (f, part) not in seen
             seen.add((f, part))
-            parts[part, f, k_idx] = blk.reshape(-1)
+            parts[part, f, k_idx.reshape(-1)] = blk.reshape(-1)
     assert len(seen) == 72
     np.testing.assert_allclose(parts.sum(0), fn, rtol=2.0**-22, atol=0)
     assert np.all(np.abs(parts[1]) <= np.abs(fn) * 2.0**-8) and np.all(np.abs(parts[2]) <= np.abs(fn) * 2.0**-16)

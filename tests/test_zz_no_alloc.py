@@ -54,8 +54,8 @@ def test_noalloc_matches_post_pre_on_two_calls(sites):
 def test_noalloc_limits(sites):
     attn, ffn = sites
     L = _lib.lib()
-    M = ops.NOALLOC_MAX_ROWS + 1
     H = gu.H
+    M = ops.noalloc_max_rows(H) + 1
     stream = torch.cuda.current_stream().cuda_stream
     # too many rows: refused before anything is enqueued (no buffer is read, so none is passed
     # beyond pointers that are never dereferenced)
