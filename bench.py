@@ -14,7 +14,7 @@ runs hc_post then hc_pre. The metric's timed region has no events inside the ste
 
 Prints one JSON line: rows/s of the whole step, the HBM roofline of the dominant kernel and the
 CPU oracle's rows/s on a bounded sample of the same workload. The dominant kernel (the fused
-path's hc_post_stats, i.e. pipe_kernel<true>; or hc_post) is timed in a region of its own:
+path's hc_post_stats, i.e. stats_kernel<10, true>; or hc_post) is timed in a region of its own:
 K back-to-back launches on the rotating input sets between one pair of HIP events recorded on
 the stream it runs on, divided by K. The roofline's "traffic" is the HBM byte count that
 rocprofv3's FETCH_SIZE / WRITE_SIZE counters gave for that kernel; it is read from the summary
@@ -53,7 +53,7 @@ PRE_BYTES_CALL = FN_BYTES + 2 * H  # fn and the norm weight, once per call
 STEP_BYTES = M_BENCH * (POST_BYTES_ROW + PRE_BYTES_ROW) + PRE_BYTES_CALL
 # the dominant kernel of each path and the algorithmic bytes one launch moves
 ROOFLINE_KERNEL = {
-    "fused": ("pipe_kernel<true> (hc_post_stats)", M_BENCH * POST_BYTES_ROW + FN_BYTES,
+    "fused": ("stats_kernel<10,true> (hc_post_stats)", M_BENCH * POST_BYTES_ROW + FN_BYTES,
               ["hc_pipe.hip", "hc_device.h", "hc_launch.h"]),
     "unfused": ("post_kernel (hc_post)", M_BENCH * POST_BYTES_ROW,
                 ["hc_post.hip", "hc_device.h", "hc_launch.h"]),
@@ -69,18 +69,41 @@ def kernel_source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel: str, files):
-    """HBM bytes per launch of `kernel` from a profiles/ summary line
-    `traffic-record: kernel=<name> M=4096 source=<hash> bytes=<n>`, if its hash is current."""
+def recorded_traffic(kernel: str, files, M: int = M_BENCH):
+    """HBM bytes per launch of `kernel` on M rows from a profiles/ summary line
+    `traffic-record: kernel=<name> M=<M> source=<hash> bytes=<n>`, if its hash is current."""
     want = kernel_source_hash(files)
     pat = re.compile(r"traffic-record: kernel=(\S+) M=(\d+) source=(\w+) bytes=(\d+)")
     name = kernel.split()[0]
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(path) as fh:
             for m in pat.finditer(fh.read()):
-                if m.group(1) == name and int(m.group(2)) == M_BENCH and m.group(3) == want:
+                if m.group(1) == name and int(m.group(2)) == M and m.group(3) == want:
                     return int(m.group(4))
     return None
+
+
+def trace_regions(csv_path: str, steps: int, kernels) -> list:
+    """Per-region average durations from a rocprofv3 kernel trace (`*_kernel_trace.csv`) of a
+    bench run with --steps `steps`. For each kernel name in `kernels` (matched with spaces
+    removed, e.g. "stats_kernel<10,true>"), its dispatches in start order end with the K
+    back-to-back launches timed for the roofline (K = steps), preceded by the K launches of the
+    timed step region; both averages are returned with the average over all its dispatches."""
+    import csv
+    out = []
+    with open(csv_path, newline="") as fh:
+        rows = list(csv.DictReader(fh))
+    for name in kernels:
+        d = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+                   if name in r["Kernel_Name"].replace(" ", ""))
+        us = [(e - b) / 1000.0 for b, e in d]
+        rec = {"kernel": name, "dispatches": len(us),
+               "all_avg_us": sum(us) / len(us) if us else None}
+        if len(us) >= 2 * steps:
+            rec["step_region_avg_us"] = sum(us[-2 * steps:-steps]) / steps
+            rec["back_to_back_avg_us"] = sum(us[-steps:]) / steps
+        out.append(rec)
+    return out
 
 
 def cpu_baseline(rows: int, target_s: float):
@@ -334,11 +357,12 @@ def chain_workload(args, torch, ops, inputs, d) -> int:
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     nbytes = M * wl["row_bytes"] + wl["call_bytes"]
 
-    # the dominant kernel (pipe_kernel<true>, the fused post + mix stats) back to back
+    # the dominant kernel (stats_kernel<10, true>, the fused post + mix stats) back to back
     def post_stats(k):
         R, x, o = sets[k % len(sets)]
         ops.post_stats(x, R, o["post1"], o["comb1"], fnp_f, out=o["R1"], workspace=o["ws"])
     kms = back_to_back_ms(torch, post_stats, args.steps)
+    kname, _, kfiles = ROOFLINE_KERNEL["fused"]
     kbytes = M * POST_BYTES_ROW + FN_BYTES
     gbs = nbytes / (ms * 1e-3) / 1e9
     print(json.dumps({
@@ -347,10 +371,12 @@ def chain_workload(args, torch, ops, inputs, d) -> int:
         "algorithmic_bytes_step": nbytes, "algorithmic_gbps_step": gbs,
         "algorithmic_frac_step": gbs / PEAK_HBM_GBS,
         "ideal_us_at_peak": nbytes / (PEAK_HBM_GBS * 1e9) * 1e6,
-        "roofline": {"kernel": "pipe_kernel<true> (hc_post_stats)", "bound": "hbm",
+        "roofline": {"kernel": kname, "bound": "hbm",
                      "ms": kms, "achieved": kbytes / (kms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": kbytes / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                     "algorithmic_bytes": kbytes},
+                     "algorithmic_bytes": kbytes,
+                     "traffic": recorded_traffic(kname, kfiles, M),
+                     "source": kernel_source_hash(kfiles)},
         "input_sets": len(sets),
     }), flush=True)
     return 0
@@ -379,7 +405,22 @@ def main() -> int:
     ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
                     help="fused: hc_post_pre (post with the next pre's mix stats in one pass, "
                          "then the pre finish); unfused: hc_post then hc_pre")
+    ap.add_argument("--trace-regions", metavar="CSV",
+                    help="no GPU work: read a rocprofv3 kernel trace of a bench run made with the "
+                         "same --steps / --path / --workload and print, per kernel of the step, "
+                         "its average duration in the timed step region and in the back-to-back "
+                         "region the roofline is taken from")
     args = ap.parse_args()
+    if args.trace_regions:
+        if args.workload != "step":  # the chains time only their dominant kernel back to back
+            names = ["stats_kernel<10,true>"]
+        elif args.path == "fused":
+            names = ["stats_kernel<10,true>", "pre_finish_kernel<10,"]
+        else:
+            names = ["post_kernel", "stats_kernel<10,false>", "pre_finish_kernel<10,"]
+        for rec in trace_regions(args.trace_regions, args.steps, names):
+            print(json.dumps(rec))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the mHC path is row-local and the library has no "
               "multi-GPU leg (rows would shard across GPUs with no exchange inside the path).",
@@ -432,7 +473,7 @@ def main() -> int:
                     workspace=o["ws"])
 
     def first_kernel(k):
-        """The dominant kernel alone: hc_post_stats (pipe_kernel<true>) or hc_post."""
+        """The dominant kernel alone: hc_post_stats (stats_kernel<10, true>) or hc_post."""
         R, x, post, comb, o = sets[k % len(sets)]
         if args.path == "fused":
             ops.post_stats(x, R, post, comb, fnp_f, out=o["R1"], workspace=o["ws"])
@@ -471,11 +512,11 @@ def main() -> int:
     kname, kbytes, kfiles = ROOFLINE_KERNEL[args.path]
     k_gbs = kbytes / (first_ms * 1e-3) / 1e9
     if args.path == "fused":
-        kernels_ms = {"hc_post_stats (pipe_kernel<true>)": first_ms,
+        kernels_ms = {"hc_post_stats (stats_kernel<10,true>)": first_ms,
                       "hc_pre_finish (pre_finish_kernel)": second_ms}
     else:
         kernels_ms = {"hc_post (post_kernel)": first_ms,
-                      "hc_pre (pipe_kernel<false> + pre_finish_kernel)": second_ms}
+                      "hc_pre (stats_kernel<10,false> + pre_finish_kernel)": second_ms}
     rows_s = M / (ms_step * 1e-3)
     step_gbs = STEP_BYTES / (ms_step * 1e-3) / 1e9
     result = {

@@ -190,7 +190,10 @@ __global__ __launch_bounds__(512) void stats_kernel(PipeArgs a) {
       u = i - lr * UR;
     };
     auto issue = [&](int k, u32x4 (&d)[kItems][kLoads]) __attribute__((always_inline)) {
-      const int g = group_of(min(k, total - 1));  // past the end: the last stage again (unused)
+      // past the last stage the same loads go out with out-of-range offsets in every lane:
+      // the instruction stream (and so the in-order wait counts) stays the same, no bytes move
+      const bool past = k >= total;
+      const int g = group_of(min(k, total - 1));
       const int r0 = g * kGroupRows;
       const __amdgpu_buffer_rsrc_t rR = group_rsrc(a.R + (int64_t)r0 * a.ldR, a.ldR);
       const __amdgpu_buffer_rsrc_t rX = group_rsrc(kPost ? a.x + (int64_t)r0 * a.ldX : a.R, kPost ? a.ldX : a.ldR);
@@ -200,11 +203,12 @@ __global__ __launch_bounds__(512) void stats_kernel(PipeArgs a) {
         bool live;
         item(t, lr, u, live);
         const int row = min(r0 + lr, M - 1) - r0;  // rows past the end read row M-1
-        const uint32_t oR = live ? (uint32_t)((row * a.ldR + hs + 8 * u) * 2) : kOutOfRange;
+        const bool go = live && !past;
+        const uint32_t oR = go ? (uint32_t)((row * a.ldR + hs + 8 * u) * 2) : kOutOfRange;
 #pragma unroll
         for (int i = 0; i < kHC; ++i) d[t][i] = buf_load(rR, oR, (uint32_t)(i * H * 2));
         if constexpr (kPost) {
-          const uint32_t oX = live ? (uint32_t)((row * a.ldX + hs + 8 * u) * 2) : kOutOfRange;
+          const uint32_t oX = go ? (uint32_t)((row * a.ldX + hs + 8 * u) * 2) : kOutOfRange;
           d[t][kHC] = buf_load(rX, oX, 0u);
         }
       }
