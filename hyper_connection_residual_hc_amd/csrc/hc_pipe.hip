@@ -25,9 +25,12 @@
 //    16-row group across the whole slice width (row runs of W bf16 = 640 bytes per stream at
 //    H = 5120); each wave loads 16 NC (row, 8-column) items with buffer loads, 2.5 wave-wide
 //    loads per array at NC = 10 (the half one reads out of range in lanes 32-63: no traffic,
-//    no branch, so the compiler's in-order load counts stay exact), two stages ahead; in the
-//    fused form it computes R' in the same operation order as the hc post kernel (identical
-//    bits) and stores it; it writes the stage's bf16 rows into one slot of a two-slot LDS ring;
+//    no branch, so the compiler's in-order load counts stay exact); in the fused form it
+//    computes R' in the same operation order as the hc post kernel (identical bits) and stores
+//    it; it writes the stage's bf16 rows into one slot of a two-slot LDS ring. Each item's loads
+//    for the next stage go out as soon as the item is done: a steady stream of about one stage
+//    (51 KB per CU in the fused form) in flight. Whole stages issued two ahead keep twice that
+//    in flight in bursts and measured slower;
 //  * waves 4-7 multiply the previous stage: wave q owns stream q, NC chunks x 6 MFMAs into one
 //    16-row accumulator set, then writes it to a double-buffered LDS epilogue; a stage later
 //    the four waves sum the streams' accumulators (stream order) and store the slice's partial
@@ -189,31 +192,30 @@ __global__ __launch_bounds__(512) void stats_kernel(PipeArgs a) {
       lr = i / UR;
       u = i - lr * UR;
     };
-    auto issue = [&](int k, u32x4 (&d)[kItems][kLoads]) __attribute__((always_inline)) {
-      // past the last stage the same loads go out with out-of-range offsets in every lane:
-      // the instruction stream (and so the in-order wait counts) stays the same, no bytes move
+    // item t of stage k into d[t]; past the last stage the same loads go out with out-of-range
+    // offsets in every lane: the instruction stream (and so the in-order wait counts) stays the
+    // same, no bytes move
+    auto issue_item = [&](int k, int t, u32x4 (&d)[kItems][kLoads]) __attribute__((always_inline)) {
       const bool past = k >= total;
       const int g = group_of(min(k, total - 1));
       const int r0 = g * kGroupRows;
       const __amdgpu_buffer_rsrc_t rR = group_rsrc(a.R + (int64_t)r0 * a.ldR, a.ldR);
       const __amdgpu_buffer_rsrc_t rX = group_rsrc(kPost ? a.x + (int64_t)r0 * a.ldX : a.R, kPost ? a.ldX : a.ldR);
+      int lr, u;
+      bool live;
+      item(t, lr, u, live);
+      const int row = min(r0 + lr, M - 1) - r0;  // rows past the end read row M-1
+      const bool go = live && !past;
+      const uint32_t oR = go ? (uint32_t)((row * a.ldR + hs + 8 * u) * 2) : kOutOfRange;
 #pragma unroll
-      for (int t = 0; t < kItems; ++t) {
-        int lr, u;
-        bool live;
-        item(t, lr, u, live);
-        const int row = min(r0 + lr, M - 1) - r0;  // rows past the end read row M-1
-        const bool go = live && !past;
-        const uint32_t oR = go ? (uint32_t)((row * a.ldR + hs + 8 * u) * 2) : kOutOfRange;
-#pragma unroll
-        for (int i = 0; i < kHC; ++i) d[t][i] = buf_load(rR, oR, (uint32_t)(i * H * 2));
-        if constexpr (kPost) {
-          const uint32_t oX = go ? (uint32_t)((row * a.ldX + hs + 8 * u) * 2) : kOutOfRange;
-          d[t][kHC] = buf_load(rX, oX, 0u);
-        }
+      for (int i = 0; i < kHC; ++i) d[t][i] = buf_load(rR, oR, (uint32_t)(i * H * 2));
+      if constexpr (kPost) {
+        const uint32_t oX = go ? (uint32_t)((row * a.ldX + hs + 8 * u) * 2) : kOutOfRange;
+        d[t][kHC] = buf_load(rX, oX, 0u);
       }
     };
-    auto produce = [&](int k, u32x4 (&d)[kItems][kLoads]) __attribute__((always_inline)) {
+    // stage k from d; right after each item, the same item of stage kn goes out into dn
+    auto produce = [&](int k, u32x4 (&d)[kItems][kLoads], int kn, u32x4 (&dn)[kItems][kLoads]) __attribute__((always_inline)) {
       const int r0 = group_of(k) * kGroupRows;
       u32x4* slot = ring[k & 1];
       // (the stats-only form stores nothing; its descriptor is never used)
@@ -263,26 +265,26 @@ __global__ __launch_bounds__(512) void stats_kernel(PipeArgs a) {
 #pragma unroll
           for (int j = 0; j < kHC; ++j) slot[lr * UPR + ((j * UR + u) ^ lr)] = st[j];
         }
+        issue_item(kn, t, dn);
       }
     };
 
-    issue(0, ld0);
-    issue(1, ld1);
+#pragma unroll
+    for (int t = 0; t < kItems; ++t) issue_item(0, t, ld0);
     __syncthreads();  // the first group's coefficients are in LDS
-    // Stages in pairs (two load buffers in fixed registers); stage k's loads were issued two
-    // stages earlier. Every path from one stage to the next issues the same memory operations,
-    // so the compiler's in-order wait counts stay exact.
+    // Stages in pairs (two load buffers in fixed registers); stage k's items were issued one
+    // by one during stage k - 1, each as soon as its slot was free, so about one stage of
+    // loads is in flight per wave at any time. Every path from one stage to the next issues the
+    // same memory operations, so the compiler's in-order wait counts stay exact.
     int k = 0;
     for (; k + 2 <= total; k += 2) {
-      produce(k, ld0);
-      issue(k + 2, ld0);
+      produce(k, ld0, k + 1, ld1);
       __syncthreads();
-      produce(k + 1, ld1);
-      issue(k + 3, ld1);
+      produce(k + 1, ld1, k + 2, ld0);
       __syncthreads();
     }
     if (k < total) {
-      produce(k, ld0);
+      produce(k, ld0, k + 1, ld1);
       __syncthreads();
     }
     __syncthreads();  // the MFMA waves' last stage: total + 2 barriers in all, as theirs
