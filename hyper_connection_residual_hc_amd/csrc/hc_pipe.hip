@@ -305,26 +305,45 @@ __global__ __launch_bounds__(512) void stats_kernel(PipeArgs a) {
     // post / comb of stage k's 16 rows (fused form): 80 of the 256 lanes each load one vector
     // of 4 (16 rows x 5) two iterations before the producers need it, and store it into
     // coefficient slot k & 1 one iteration later, so the load's latency stays off the stage.
+    // Every memory operation of these waves is a buffer access that every lane issues in every
+    // iteration (lanes and stages without work use out-of-range offsets: no traffic), so the
+    // compiler's in-order wait before the coefficient store counts only what was issued after
+    // the load instead of draining the partial stores of the stage before.
     const int cv = threadIdx.x - 256;
     const int clr = cv / 5, cc4 = cv - (cv / 5) * 5;
     const bool coef_lane = cv < kGroupRows * 5;
     auto coef_load = [&](int k) __attribute__((always_inline)) {
-      const int row = min(group_of(min(k, total - 1)) * kGroupRows + clr, M - 1);
-      const float* src = cc4 == 0 ? a.post + (int64_t)row * kHC : a.comb + (int64_t)row * 16 + 4 * (cc4 - 1);
-      return coef_lane ? *reinterpret_cast<const f32x4*>(src) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r0 = group_of(min(k, total - 1)) * kGroupRows;
+      const int row = min(r0 + clr, M - 1) - r0;
+      const bool go = coef_lane && k < total;
+      const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(a.post + (int64_t)r0 * kHC), (short)0, kGroupRows * kHC * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(a.comb + (int64_t)r0 * kHC * kHC), (short)0, kGroupRows * kHC * kHC * 4, 0x00020000);
+      const uint32_t oP = go && cc4 == 0 ? (uint32_t)(row * kHC * 4) : kOutOfRange;
+      const uint32_t oC = go && cc4 != 0 ? (uint32_t)(row * kHC * kHC * 4 + (cc4 - 1) * 16) : kOutOfRange;
+      const u32x4 vp = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rP, oP, 0u, 0));
+      const u32x4 vc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rC, oC, 0u, 0));
+      return vp | vc;  // the out-of-range one reads zero bits
     };
-    auto coef_store = [&](int k, const f32x4& v) __attribute__((always_inline)) {
-      if (coef_lane && k < total) *reinterpret_cast<f32x4*>(&coef[k & 1][clr][4 * cc4]) = v;
+    auto coef_store = [&](int k, const u32x4& v) __attribute__((always_inline)) {
+      if (coef_lane && k < total) *reinterpret_cast<u32x4*>(&coef[k & 1][clr][4 * cc4]) = v;
     };
-    // the four streams' accumulators of stage k, summed in stream order, into the partials
+    // the four streams' accumulators of stage k, summed in stream order, into the partials;
+    // k < 0: nothing is stored (the same instructions, out-of-range offsets)
     auto flush = [&](int k) __attribute__((always_inline)) {
-      const int r0 = group_of(k) * kGroupRows;
-      const auto& ep = epi[k & 1];
-      for (int idx = threadIdx.x - 256; idx < kGroupRows * (kMix + 1); idx += 256) {
-        const int row = idx / (kMix + 1);
-        const int f = idx - row * (kMix + 1);
-        const int grow = r0 + row;
-        if (grow >= M) continue;
+      const int kk = max(k, 0);
+      const int r0 = group_of(kk) * kGroupRows;
+      const auto& ep = epi[kk & 1];
+      const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc(
+          a.part + ((int64_t)s * M + r0) * kPartStride, (short)0, kGroupRows * kPartStride * 4, 0x00020000);
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int idx = cv + 256 * it;  // 16 rows x 25 values = 400 < 512
+        const bool in = idx < kGroupRows * (kMix + 1);
+        const int id = in ? idx : 0;
+        const int row = id / (kMix + 1);
+        const int f = id - row * (kMix + 1);
         float v = 0.0f;
         if (f < 16) {
 #pragma unroll
@@ -336,7 +355,8 @@ __global__ __launch_bounds__(512) void stats_kernel(PipeArgs a) {
 #pragma unroll
           for (int w = 0; w < kHC; ++w) v += ep[w][row][32];
         }
-        a.part[((int64_t)s * M + grow) * kPartStride + f] = v;
+        const bool go = k >= 0 && in && r0 + row < M;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rO, go ? (uint32_t)(id * 4) : kOutOfRange, 0u, 0);
       }
     };
     // stage k's MFMAs from its ring slot, accumulators to epilogue slot k & 1 (16x16 layout:
@@ -363,7 +383,7 @@ __global__ __launch_bounds__(512) void stats_kernel(PipeArgs a) {
       }
     };
 
-    f32x4 cnext = {0.f, 0.f, 0.f, 0.f}, cnext2 = cnext;
+    u32x4 cnext = {0u, 0u, 0u, 0u};
     if (kPost) {
       coef_store(0, coef_load(0));
       cnext = coef_load(1);
@@ -371,15 +391,14 @@ __global__ __launch_bounds__(512) void stats_kernel(PipeArgs a) {
     __syncthreads();  // matches the producers' first barrier
     // Iteration i: the coefficients of stage i + 1 into LDS (loaded an iteration earlier) and
     // the load of stage i + 2's, the partials of stage i - 2 (epilogue written in iteration
-    // i - 1), the MFMAs of stage i - 1 (ring slot written by the producers in iteration i - 1);
-    // then the block barrier.
+    // i - 1; none for i < 2), the MFMAs of stage i - 1 (ring slot written by the producers in
+    // iteration i - 1); then the block barrier.
     for (int i = 0; i <= total; ++i) {
       if (kPost) {
         coef_store(i + 1, cnext);
-        cnext2 = coef_load(i + 2);
-        cnext = cnext2;
+        cnext = coef_load(i + 2);
       }
-      if (i >= 2) flush(i - 2);
+      flush(i - 2);
       if (i >= 1) mma(i - 1);
       __syncthreads();
     }
