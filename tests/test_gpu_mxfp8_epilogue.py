@@ -99,6 +99,32 @@ def test_pre_mxfp8_row_slices_are_bit_identical(sites):
             assert _bits_equal(part[k], full[k][lo:hi]), (k, lo, hi)
 
 
+@pytest.mark.parametrize("Hs,M", [(1024, 70), (3072, 33), (6144, 130), (8192, 17)])
+def test_mxfp8_epilogue_at_other_widths(Hs, M):
+    """The finish's MXFP8 epilogue compiled for other row widths (2 to 16 column blocks of 512
+    per lane; 32 to 256 scale blocks per row): the fused pre and the fused post -> pre give
+    the standalone quantizer's bytes of their own bf16 y, and those are the oracle's MXFP8 of
+    that y."""
+    gu.say(f"MXFP8 epilogue H={Hs} M={M}")
+    site = gu.Site(41, 42, H_=Hs)
+    nxt = gu.Site(43, 44, H_=Hs)
+    R = gu.dev(inputs.residual(M, 45, H=Hs))
+    x = gu.dev(inputs.sublayer_out(M, 46, H=Hs))
+    y, post, comb, _ = ops.pre(R, site.fnp, site.scale_d, site.base_d, site.w_d)
+    y2, q, sc, post2, comb2, _ = ops.pre_mxfp8(R, site.fnp, site.scale_d, site.base_d, site.w_d)
+    assert _bits_equal(y2, y) and torch.equal(post2, post) and torch.equal(comb2, comb)
+    q_ref, s_ref = ops.mxfp8_quant_rows(y)
+    assert torch.equal(q, q_ref) and torch.equal(sc, s_ref)
+    oq, osc = o.mxfp8_quant_rows(gu.bits_of(y))
+    assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(sc.cpu().numpy(), osc)
+    Rn, yn, _, _, _ = ops.post_pre(x, R, post, comb, nxt.fnp, nxt.scale_d, nxt.base_d, nxt.w_d)
+    Rm, (ym, qm, sm, _, _, _) = ops.post_pre_mxfp8(x, R, post, comb, nxt.fnp, nxt.scale_d,
+                                                   nxt.base_d, nxt.w_d)
+    assert _bits_equal(Rm, Rn) and _bits_equal(ym, yn)
+    oq2, osc2 = o.mxfp8_quant_rows(gu.bits_of(yn))
+    assert np.array_equal(qm.cpu().numpy(), oq2) and np.array_equal(sm.cpu().numpy(), osc2)
+
+
 def test_mxfp8_epilogue_argument_checks(sites):
     attn, _ = sites
     M = 8

@@ -347,8 +347,9 @@ def test_binding_rejects_short_outputs(attn, ffn):
 
 @pytest.mark.parametrize("Hs", [2048, 3072, 4096, 6144, 7168, 8192])
 def test_wider_hidden_sizes(Hs):
-    """Other row widths (4 to 16 column blocks of 512 per lane; as many stages per slice): pre
-    and post vs the oracle, the fused op vs post then pre."""
+    """Other row widths: 4 to 16 column blocks of 512 per lane in the finish, and in the stats
+    kernel 8 (H = 2048) to 32 (H = 8192) column slices of 256 columns per stream. The pre and
+    the post vs the oracle, the fused op vs post then pre."""
     gu.say(f"H={Hs}")
     site = gu.Site(15, 16, H_=Hs)
     nxt = gu.Site(17, 18, H_=Hs)
@@ -398,11 +399,10 @@ def test_combine_norm_and_post_at_odd_block_counts(Hs):
 
 
 def test_narrowest_hidden_size_two_stages_per_slice():
-    """H = 1024: each slice is two stages, the fewest the stats kernels take, so tiles end on
-    every other stage (back-to-back epilogues; in the stats-only form the two tiles of a pair
-    end on consecutive stages). At M = 6161 every block runs several tiles (pairs and a lone
-    tile; in the fused form tiles one after another): the pre vs the oracle on sampled rows,
-    and the fused op vs post then pre, bit for bit."""
+    """H = 1024, the narrowest width with mix stats: 8 column slices of 128 columns per stream
+    (NC = 4, one full wave-wide item per array and producer wave), 32 blocks per slice. At
+    M = 6161 (386 row groups, the last one ragged) the blocks run 12 or 13 stages each: the pre
+    vs the oracle on sampled rows, and the fused op vs post then pre, bit for bit."""
     Hs, M = 1024, 6161
     gu.say(f"H={Hs} M={M}")
     site = gu.Site(21, 22, H_=Hs)
