@@ -18,10 +18,9 @@
  * - M == 0 is a successful no-op. A row slice [a, b) of a call is the same call with every
  *   row pointer advanced by a rows and M = b - a; the library takes no "logical row count",
  *   and every row's result is bit-identical whether the row is computed in a full call or in
- *   any slice (mxfp8_swizzle_128x4, a layout over the whole of M, is the one exception). The
- *   one choice keyed on M is which kernel computes the mix stats: calls of up to 1024 rows
- *   (decode, verify, short prefill; H up to 8192) take a one-pass kernel with lower latency
- *   whose results are the same bits as the pipelined kernel's.
+ *   any slice (mxfp8_swizzle_128x4, a layout over the whole of M, is the one exception). One
+ *   kernel computes the mix stats at every M (decode-sized calls launch fewer blocks), so no
+ *   step of a row's arithmetic depends on M.
  * - Return value: HC_OK (0) or one of the HC_ERR_* codes below; hc_status_string() names it.
  *   An error return means nothing was enqueued.
  *
@@ -71,7 +70,7 @@ HC_API int hc_abi_version(void);
  *
  * fn:        fp32 [24, 4H] row-major (device).
  * fn_packed: hc_fn_packed_bytes(H) bytes (device, 16-byte aligned), written.
- * H:         multiple of 1024.
+ * H:         multiple of 1024, at most 8192.
  * ------------------------------------------------------------------------------------- */
 HC_API size_t hc_fn_packed_bytes(int32_t H);
 HC_API int hc_fn_pack(const float* fn, int32_t H, uint16_t* fn_packed, void* stream);
@@ -87,7 +86,7 @@ HC_API int hc_fn_pack(const float* fn, int32_t H, uint16_t* fn_packed, void* str
  * sumsq:      fp32 [M] or NULL, written when given.
  * workspace:  >= hc_pre_stats_workspace_bytes(M, H) bytes of device memory, 256-byte aligned;
  *             its contents on entry do not matter.
- * H:          multiple of 1024.
+ * H:          multiple of 1024, at most 8192.
  * ------------------------------------------------------------------------------------- */
 HC_API size_t hc_pre_stats_workspace_bytes(int64_t M, int32_t H);
 HC_API int hc_pre_stats(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, int64_t M,

@@ -77,8 +77,9 @@ def test_head_zero_scale_and_slices(head):
 
 @pytest.mark.parametrize("Hs,M", [(3072, 130), (6144, 70), (1024, 1100)])
 def test_head_other_widths(Hs, M):
-    """Other row widths (6 and 12 column blocks per lane; two stages per slice with the
-    pipelined kernel at 1100 rows) against the oracle."""
+    """Other row widths against the oracle: 6 and 12 column blocks per lane in the head's
+    finish, and at H = 1024 the stats kernel's narrowest geometry (8 slices of 128 columns per
+    stream, 32 blocks per slice running 2 or 3 stages at 1100 rows)."""
     gu.say(f"hc_head H={Hs} M={M}")
     fn, scale, base = inputs.hc_head_params(inputs.SEED_HEAD + 1, H=Hs)
     R = inputs.residual(M, M + 7, H=Hs)

@@ -479,8 +479,9 @@ def _wide_bf16(M, inner, pad):
 
 def test_padded_row_strides_fused_and_separate(attn, ffn):
     """Every bf16 row argument of hc_pre, hc_post and hc_post_pre as a view into wider rows
-    (a different pad for each), at a size where blocks run two and three 64-row tiles and the
-    last one is ragged: the same bits as the contiguous calls, and no pad byte written."""
+    (a different pad for each), at a size where the stats blocks run 16 or 17 stages of 16 rows
+    and the last group is ragged (M = 4177: 261 full groups and one row): the same bits as the
+    contiguous calls, and no pad byte written."""
     M, H = 4177, gu.H
     gu.say(f"padded strides M={M}")
     R = gu.dev(inputs.residual(M, 91))
@@ -519,9 +520,10 @@ def test_padded_row_strides_fused_and_separate(attn, ffn):
 
 def test_full_size_post_pre_matches_oracle_on_sampled_rows(attn, ffn):
     """The measured step itself: hc_post_pre at M = 4096, H = 5120 in the launch the throughput
-    benchmark times (256 blocks of two 64-row tiles each), against the oracle's post followed by
-    its pre on sampled rows: every tile's first and last row, the first and last 70 rows, and
-    200 drawn at random. post and comb come from the oracle's pre of the attention site."""
+    benchmark times (256 blocks, 16 per column slice, each running 16 stages of one 16-row
+    group), against the oracle's post followed by its pre on sampled rows: every row group's
+    first and last row, the first and last 70 rows, and 200 drawn at random. post and comb come
+    from the oracle's pre of the attention site."""
     M = 4096
     gu.say(f"hc_post_pre full size M={M} sampled")
     R = inputs.residual(M, 4096 + 11)
@@ -535,7 +537,7 @@ def test_full_size_post_pre_matches_oracle_on_sampled_rows(attn, ffn):
         out=(_poison_bf16(M, 4, gu.H), _poison_bf16(M, gu.H), _poison_f32(M, 4),
              _poison_f32(M, 4, 4), _poison_f32(M, 4)))
     rng = np.random.default_rng(4096)
-    edges = np.concatenate([np.arange(0, M, 64), np.arange(63, M, 64)])
+    edges = np.concatenate([np.arange(0, M, 16), np.arange(15, M, 16)])
     rows = np.unique(np.concatenate([edges, np.arange(70), np.arange(M - 70, M),
                                      rng.choice(M, 200, replace=False)]))
     oR1, oR1_bits = o.hc_post(inputs.bits(x)[rows], inputs.bits(R)[rows], post32.numpy()[rows],

@@ -16,7 +16,7 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 M_BIG = 1100  # several row groups on every block of a slice
-# slices of 1 .. 1024 rows: one and several 16-row groups, ragged last groups, tile boundaries,
+# slices of 1 .. 1024 rows: one and several 16-row groups, ragged last groups, group boundaries,
 # odd offsets, the last rows
 SLICES = [(0, 1), (0, 16), (3, 5), (7, 15), (31, 39), (48, 64), (63, 65), (1, 18), (70, 177),
           (333, 433), (5, 1029), (76, 1100), (1099, 1100)]
