@@ -428,6 +428,43 @@ def test_narrowest_hidden_size_two_stages_per_slice():
     assert torch.equal(full[2], post2) and torch.equal(full[3], comb2)
 
 
+def test_widest_hidden_size_many_stages():
+    """H = 8192, the widest width with mix stats: 32 column slices of 256 columns per stream,
+    8 blocks per slice. At M = 2500 (157 row groups, the last one of 4 rows) every block runs
+    19 or 20 stages: the fused op vs post then pre bit for bit, and the pre and the post vs the
+    oracle on sampled rows (every group's edges at both ends, random rows)."""
+    Hs, M = 8192, 2500
+    gu.say(f"H={Hs} M={M}")
+    site = gu.Site(51, 52, H_=Hs)
+    nxt = gu.Site(53, 54, H_=Hs)
+    R = inputs.residual(M, 55, H=Hs)
+    x = inputs.sublayer_out(M, 56, H=Hs)
+    Rd, xd = gu.dev(R), gu.dev(x)
+    y, post, comb, pre = ops.pre(Rd, site.fnp, site.scale_d, site.base_d, site.w_d,
+                                 want_pre=True)
+    full = ops.post_pre(xd, Rd, post, comb, nxt.fnp, nxt.scale_d, nxt.base_d, nxt.w_d)
+    Rn = ops.post(xd, Rd, post, comb)
+    y2, post2, comb2, _ = ops.pre(Rn, nxt.fnp, nxt.scale_d, nxt.base_d, nxt.w_d)
+    assert torch.equal(full[0].view(torch.int16), Rn.view(torch.int16))
+    assert torch.equal(full[1].view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(full[2], post2) and torch.equal(full[3], comb2)
+    rng = np.random.default_rng(8192)
+    rows = np.unique(np.concatenate([np.arange(0, 160, 16), np.arange(15, 160, 16),
+                                     np.arange(M - 40, M), rng.choice(M, 60, replace=False)]))
+    ridx = torch.from_numpy(rows).to(gu.DEV)
+    ref = site.oracle_pre(inputs.bits(R)[rows])
+    gu.assert_coef_close(gu.f32_np(pre[ridx]), ref["pre"], "pre")
+    gu.assert_coef_close(gu.f32_np(comb[ridx]), ref["comb"], "comb")
+    gu.assert_bf16_close(gu.bits_of(y[ridx]), ref["y"], "y")
+    oR, _ = o.hc_post(inputs.bits(x)[rows], inputs.bits(R)[rows], gu.f32_np(post)[rows],
+                      gu.f32_np(comb)[rows])
+    gu.assert_bf16_close(gu.bits_of(Rn[ridx]), oR, "R'")
+    ref2 = nxt.oracle_pre(gu.bits_of(Rn[ridx]))
+    gu.assert_coef_close(gu.f32_np(comb2[ridx]), ref2["comb"], "comb (next site)")
+    gu.assert_coef_close(gu.f32_np(post2[ridx]), ref2["post"], "post (next site)")
+    gu.assert_bf16_close(gu.bits_of(y2[ridx]), ref2["y"], "y (next site)")
+
+
 def test_graph_capture_replays_match_eager(attn, ffn):
     """The fused step captured in a HIP graph (the entry points allocate nothing and clear no
     memory, so they capture as plain kernel nodes): three replays, with unrelated eager work
