@@ -116,6 +116,68 @@ def _split_sinkhorn_without_sinkhorn_eps(mixes, scale, base, hc=4, iters=20, eps
     return pre, post, _real_sinkhorn(logits, iters, 0.0)
 
 
+def _stats_over_h(R_bits, fn, rms_eps=1e-6):
+    """The RMS scale over one stream's width H instead of the flattened 4H."""
+    R_bits = np.asarray(R_bits)
+    H = R_bits.shape[-1]
+    mixes, sumsq = _real_stats(R_bits, fn, rms_eps)
+    s = np.asarray(sumsq, dtype=np.float64)[:, None]
+    return mixes * np.sqrt(s / (4 * H) + rms_eps) / np.sqrt(s / H + rms_eps), sumsq
+
+
+def _post_without_x(x_bits, R_bits, post, comb):
+    """The post-weighted sublayer output term left out."""
+    return _real_post(x_bits, R_bits, np.zeros_like(np.asarray(post, dtype=np.float64)), comb)
+
+
+def _combine_norm_mean_over_4h(R_bits, pre, w_bits, eps=1e-6):
+    """The RMSNorm mean taken over 4H columns instead of the combined row's H."""
+    c = o.hc_combine(R_bits, pre)
+    w = o.bf16_to_f64(w_bits)
+    y = c / np.sqrt((c * c).sum(-1, keepdims=True) / (4 * c.shape[-1]) + eps) * w
+    return y, o.f64_to_bf16(y)
+
+
+_real_quant = o.mxfp8_quant_rows
+_real_swizzle = o.swizzle_128x4
+
+
+def _quant_block_16(y_bits, block=32):
+    return _real_quant(y_bits, 16)
+
+
+def _quant_scale_bias_128(y_bits, block=32):
+    q, sf = _real_quant(y_bits, block)
+    return q, (sf.astype(np.int64) + 1).astype(np.uint8)
+
+
+def _e4m3_nan_on_overflow(s):
+    """Overflow to the NaN code instead of saturating to +-448."""
+    s = np.asarray(s, dtype=np.float64)
+    code = _real_e4m3(np.clip(s, -448.0, 448.0))
+    nan = 0x7F | np.where(np.signbit(s), 0x80, 0)
+    return np.where(np.abs(s) > 448.0, nan, code).astype(np.uint8)
+
+
+def _swizzle_inner_swapped(sf):
+    """Inside a tile [m % 32][g % 4][(m % 128) // 32] instead of [m % 32][(m % 128) // 32][g % 4]."""
+    sf = np.asarray(sf, dtype=np.uint8)
+    M, G = sf.shape
+    mt = (M + 127) // 128
+    pad = np.zeros((mt * 128, G), dtype=np.uint8)
+    pad[:M] = sf
+    out = np.empty(mt * 128 * G, dtype=np.uint8)
+    pos = 0
+    for tm in range(mt):
+        for tg in range(G // 4):
+            for r32 in range(32):
+                for c in range(4):
+                    for r4 in range(4):
+                        out[pos] = pad[tm * 128 + r4 * 32 + r32, tg * 4 + c]
+                        pos += 1
+    return out
+
+
 def _scale_exp_floor(amax):
     amax = np.asarray(amax, dtype=np.float64)
     pos = amax > 0
@@ -142,6 +204,12 @@ def _run_all_pins():
         ("pre_zero_scale", pins.test_hc_pre_zero_scale_closed_form, ()),
         ("pre_two_streams", pins.test_hc_pre_two_streams_share_a_column, ()),
         ("split_sinkhorn_uniform", pins.test_split_sinkhorn_zero_scale_uniform_logits_closed_form, ()),
+        ("post_only", pins.test_post_only_post_term, ()),
+        ("cn_zero", pins.test_combine_norm_zero_input_gives_zero, ()),
+        ("e4m3_sat", pins.test_e4m3_saturates, ()),
+        ("mx_block", pins.test_mxfp8_block_is_32_columns_wide, ()),
+        ("swz_layout", pins.test_swizzle_128x4_places_every_byte_by_the_stated_layout, (130, 8)),
+        ("swz_hand", pins.test_swizzle_128x4_hand_positions, ()),
     ]
     for i0, h0 in [(0, 0), (2, 5), (3, 7)]:
         calls.append((f"pre_onehot_{i0}_{h0}", pins.test_hc_pre_one_nonzero_row_closed_form, (i0, h0)))
@@ -155,7 +223,8 @@ def _run_all_pins():
         calls.append((f"mx_hand_{case[2]!r}", pins.test_mxfp8_hand_cases, (case,)))
     for name, fn, args in calls:
         try:
-            fn(*args)
+            with np.errstate(all="ignore"):  # a planted mistake may divide by zero
+                fn(*args)
         except AssertionError:
             failed.append(name)
     return failed
@@ -179,6 +248,13 @@ MUTANTS = [
     ("hc_pre", _pre_norm_takes_stats_eps, "pre_"),
     ("hc_head", _head_without_rsqrt, "head_onehot"),
     ("hc_split_sinkhorn", _split_sinkhorn_without_sinkhorn_eps, "split_sinkhorn"),
+    ("hc_mix_stats", _stats_over_h, "stats_onehot"),
+    ("hc_post", _post_without_x, "post_"),
+    ("hc_combine_norm", _combine_norm_mean_over_4h, "cn_onehot"),
+    ("mxfp8_quant_rows", _quant_block_16, "mx_block"),
+    ("mxfp8_quant_rows", _quant_scale_bias_128, "mx_"),
+    ("e4m3_encode", _e4m3_nan_on_overflow, "e4m3_sat"),
+    ("swizzle_128x4", _swizzle_inner_swapped, "swz_"),
 ]
 
 

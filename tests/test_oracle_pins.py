@@ -340,6 +340,21 @@ def test_mxfp8_hand_cases(case):
     assert int(q[0, 1]) == code
 
 
+def test_mxfp8_block_is_32_columns_wide():
+    """A block's scale comes from the largest of its 32 values wherever it sits, and each 32
+    columns have a scale byte of their own. Worked by hand from the scale rule and the e4m3fn
+    format: block 0 holds 56 = 1.75 * 2^5 in column 31 and 1.0 in column 0, so e = 5 - 8 = -3
+    (byte 124), 56 codes as 448 (0x7E) and 1.0 as 8.0 (0x50); block 1 holds only 1.0 in
+    column 32, so e = -8 (byte 119) and 1.0 codes as 256 (0x78)."""
+    row = np.zeros(64)
+    row[31], row[0], row[32] = 56.0, 1.0, 1.0
+    q, sf = o.mxfp8_quant_rows(_bf16_bits_of(row)[None, :])
+    assert sf.shape == (1, 2)
+    assert (int(sf[0, 0]), int(sf[0, 1])) == (124, 119)
+    assert (int(q[0, 0]), int(q[0, 31]), int(q[0, 32])) == (0x50, 0x7E, 0x78)
+    assert np.count_nonzero(q) == 3
+
+
 def test_e4m3_encode_matches_torch_cast_over_all_bf16_patterns():
     b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     v = o.bf16_to_f64(b)
