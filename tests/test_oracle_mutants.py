@@ -138,6 +138,40 @@ def _combine_norm_mean_over_4h(R_bits, pre, w_bits, eps=1e-6):
     return y, o.f64_to_bf16(y)
 
 
+_real_f64_to_bf16 = o.f64_to_bf16
+
+
+def _f64_to_bf16_truncating(v):
+    """Rounding toward zero instead of to nearest even."""
+    v = np.asarray(v, dtype=np.float64)
+    b = v.astype(np.float32).view(np.uint32) >> np.uint32(16)
+    return np.where(np.isnan(v), np.uint16(0x7FC0), b.astype(np.uint16))
+
+
+def _f64_to_bf16_through_float32(v):
+    """Two roundings: float64 -> float32 -> bf16 (ties can land on the wrong side)."""
+    return _real_f64_to_bf16(np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64))
+
+
+def _split_pre_post_swapped(mixes, scale, base, hc=4, pre_eps=1e-6, post_mult=2.0):
+    """pre read from the post group of the mixes and post from the pre group."""
+    mixes = np.array(mixes, dtype=np.float64)
+    base = np.array(base, dtype=np.float64)
+    scale = np.array(scale, dtype=np.float64).reshape(-1)
+    mixes[:, 0:4], mixes[:, 4:8] = mixes[:, 4:8].copy(), mixes[:, 0:4].copy()
+    base[0:4], base[4:8] = base[4:8].copy(), base[0:4].copy()
+    scale[0], scale[1] = scale[1], scale[0]
+    return _real_split(mixes, scale, base, hc, pre_eps, post_mult)
+
+
+def _e4m3_flush_subnormals(s):
+    """Values below the smallest normal (2^-6) coded as zero."""
+    s = np.asarray(s, dtype=np.float64)
+    code = _real_e4m3(s)
+    zero = np.where(np.signbit(s), 0x80, 0x00)
+    return np.where(np.abs(s) < 2.0**-6, zero, code).astype(np.uint8)
+
+
 _real_quant = o.mxfp8_quant_rows
 _real_swizzle = o.swizzle_128x4
 
@@ -205,6 +239,8 @@ def _run_all_pins():
         ("pre_two_streams", pins.test_hc_pre_two_streams_share_a_column, ()),
         ("split_sinkhorn_uniform", pins.test_split_sinkhorn_zero_scale_uniform_logits_closed_form, ()),
         ("post_only", pins.test_post_only_post_term, ()),
+        ("bf16_torch", pins.test_bf16_rounding_matches_torch_on_float32_inputs, ()),
+        ("bf16_single", pins.test_bf16_rounding_is_single_rounding_from_float64, ()),
         ("cn_zero", pins.test_combine_norm_zero_input_gives_zero, ()),
         ("e4m3_sat", pins.test_e4m3_saturates, ()),
         ("mx_block", pins.test_mxfp8_block_is_32_columns_wide, ()),
@@ -255,6 +291,10 @@ MUTANTS = [
     ("mxfp8_quant_rows", _quant_scale_bias_128, "mx_"),
     ("e4m3_encode", _e4m3_nan_on_overflow, "e4m3_sat"),
     ("swizzle_128x4", _swizzle_inner_swapped, "swz_"),
+    ("f64_to_bf16", _f64_to_bf16_truncating, "bf16_"),
+    ("f64_to_bf16", _f64_to_bf16_through_float32, "bf16_single"),
+    ("hc_split", _split_pre_post_swapped, "split_"),
+    ("e4m3_encode", _e4m3_flush_subnormals, "e4m3_torch"),
 ]
 
 
