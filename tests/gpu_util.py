@@ -76,6 +76,36 @@ class Site:
                         inputs.bits(self.w))
 
 
+def assert_coef_properties(pre, post, comb, eps: float = 1e-6) -> None:
+    """What every row's coefficients satisfy, checked on all rows on the device: pre in
+    [eps, 1 + eps] (sigmoid + eps), post in [0, 2] (2 sigmoid), comb positive with every
+    destination column summing to 1 within 1e-5 (the last Sinkhorn step normalises the
+    columns: s / (s + eps))."""
+    slack = 1e-6
+    for t in (pre, post, comb):
+        assert t is None or torch.isfinite(t).all()
+    if pre is not None:
+        assert (pre >= eps - slack).all() and (pre <= 1 + eps + slack).all()
+    assert (post >= 0).all() and (post <= 2).all()
+    assert (comb > 0).all()
+    colsum = comb.double().sum(dim=1)  # comb[m, i, j] over the sources i
+    assert (colsum - 1).abs().max().item() <= 1e-5
+
+
+def assert_mxfp8_bits_match_oracle(y: torch.Tensor, q: torch.Tensor, sf: torch.Tensor,
+                                   chunk: int = 1024) -> None:
+    """q / sf equal, byte for byte on every row, the oracle's MXFP8 of the bf16 y the GPU wrote
+    (rows taken in chunks to bound host memory)."""
+    M = y.shape[0]
+    for a in range(0, M, chunk):
+        gy = bits_of(y[a:a + chunk])
+        oq, osf = o.mxfp8_quant_rows(gy)
+        gq = q[a:a + chunk].cpu().numpy()
+        gs = sf[a:a + chunk].cpu().numpy()
+        bad = np.nonzero(np.any(oq != gq, axis=1) | np.any(osf != gs, axis=1))[0]
+        assert len(bad) == 0, f"MXFP8 rows differing from the oracle: {a + bad[:8]}"
+
+
 def stats_geom(H):
     """(slices S, 32-column chunks per stream per slice NC) of the stats kernels at width H, as
     the packed layout documents it: the largest even NC <= 10 with S = H / 32 NC a multiple of

@@ -129,6 +129,13 @@ def test_config4_prefill_chunk_post_pre_mxfp8(sites):
     deq = np.ldexp(o.e4m3_decode(gq).reshape(len(rows), -1, 32), e[:, :, None])
     assert np.all(np.abs(deq - yv) <= np.maximum(np.abs(yv) * 2.0**-4, np.ldexp(2.0**-10, e)[:, :, None]))
 
+    # on all 16384 rows: the coefficients' ranges and column sums, y finite, and the MXFP8
+    # bytes equal to the oracle's quantization of the GPU's own bf16 y
+    gu.assert_coef_properties(None, post0, comb0)
+    gu.assert_coef_properties(pre2, post2, comb2)
+    assert torch.isfinite(y.float()).all()
+    gu.assert_mxfp8_bits_match_oracle(y, q, sf)
+
     # the quantizer itself on the oracle's y rows (same inputs on both sides): bit-exact
     yo = torch.from_numpy(ref2["y_bits"].view(np.int16)).view(torch.bfloat16)
     q2, s2 = ops.mxfp8_quant_rows(gu.dev(yo))

@@ -593,3 +593,6 @@ def test_full_size_post_pre_matches_oracle_on_sampled_rows(attn, ffn):
     for name, g in (("pre", pre2), ("post", post2), ("comb", comb2)):
         err = np.abs(gu.f32_np(g[ridx]) - ref2[name]).max()
         assert err <= 2e-3, f"{name} (sampled, oracle chain): {err}"
+    # properties that hold at any size, on all 4096 rows
+    gu.assert_coef_properties(pre2, post2, comb2)
+    assert torch.isfinite(y.float()).all() and torch.isfinite(Rn.float()).all()
