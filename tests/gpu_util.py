@@ -38,10 +38,15 @@ def f32_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy().astype(np.float64)
 
 
-def assert_bf16_close(gpu_bits: np.ndarray, oracle: np.ndarray, what: str) -> None:
+def assert_bf16_close(gpu_bits: np.ndarray, oracle: np.ndarray, what: str,
+                      extra: np.ndarray | None = None) -> None:
+    """|g - o| <= 2e-2 |o| + 1e-3 rms(o_row) (+ extra, an elementwise bound that a comparison
+    across differently rounded inputs derives, where it applies)."""
     g = o.bf16_to_f64(gpu_bits)
     rms = np.sqrt(np.mean(oracle * oracle, axis=-1, keepdims=True))
     bound = BF16_REL * np.abs(oracle) + BF16_ROW_ABS * rms
+    if extra is not None:
+        bound = bound + extra
     err = np.abs(g - oracle)
     bad = err > bound
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
@@ -59,6 +64,26 @@ def assert_mixes_close(gpu: np.ndarray, oracle: np.ndarray, what: str = "mixes")
 def assert_coef_close(gpu: np.ndarray, oracle: np.ndarray, what: str) -> None:
     err = np.abs(gpu - oracle)
     assert np.all(err <= COEF_ABS), f"{what}: worst abs {err.max():.3g}"
+
+
+CHAIN_COEF_ABS = 2e-3
+
+
+def chain_y_slack(R_bits: np.ndarray, pre: np.ndarray, w: torch.Tensor,
+                  coef_abs: float = CHAIN_COEF_ABS) -> np.ndarray:
+    """Elementwise bound on how far the pre's y moves between two residuals that are each a
+    bf16 rounding of the same R' (at most one ulp, 2^-7 relative, apart) read with pre weights
+    up to coef_abs apart. The combine c = sum_i pre_i R'_i then moves by up to
+    sum_i (pre_i 2^-7 + coef_abs) |R'_i|, which the norm scales by |w| rsqrt(mean(c^2) + eps);
+    the norm factor itself moves by up to 2^-7 relative. R_bits is one of the two residuals,
+    pre the oracle's pre on it."""
+    Ra = np.abs(o.bf16_to_f64(R_bits))
+    pre = np.asarray(pre, dtype=np.float64)
+    c = o.hc_combine(R_bits, pre)
+    rstd = 1.0 / np.sqrt(np.mean(c * c, axis=-1, keepdims=True) + o.RMS_EPS)
+    wa = np.abs(w.double().numpy())[None, :]
+    dc = np.einsum("mi,mih->mh", pre * 2.0**-7 + coef_abs, Ra)
+    return wa * rstd * (dc + 2.0**-7 * np.abs(c))
 
 
 class Site:

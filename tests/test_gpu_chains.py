@@ -12,7 +12,8 @@ oracle's pre of the GPU's own bf16 R' (R' itself is checked against the oracle's
 extra, the GPU chain is also compared with the oracle's whole chain: there the second pre reads
 the oracle's R', one bf16 rounding (relative 2^-8) away from the GPU's, which moves the logits
 by up to |scale| * 2^-8 * max|mixes| ~ 1e-3, so that comparison holds the coefficients to 2e-3
-absolute."""
+absolute, and y to its bar plus the shift that R' and pre differences of that size can cause
+where a row's combine cancels (gpu_util.chain_y_slack)."""
 import numpy as np
 import pytest
 import torch
@@ -23,7 +24,7 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-CHAIN_COEF_ABS = 2e-3
+CHAIN_COEF_ABS = gu.CHAIN_COEF_ABS
 
 
 @pytest.fixture(scope="module")
@@ -56,7 +57,8 @@ def test_config3_pre_post_pre_chain(sites):
     gu.assert_coef_close(gu.f32_np(post1), ref1["post"], "post attn")
     gu.assert_coef_close(gu.f32_np(comb1), ref1["comb"], "comb attn")
     gu.assert_bf16_close(gu.bits_of(R1), oR1, "R' after post")
-    gu.assert_bf16_close(gu.bits_of(y2), ref2["y"], "y ffn")
+    gu.assert_bf16_close(gu.bits_of(y2), ref2["y"], "y ffn",
+                         extra=gu.chain_y_slack(oR1_bits, ref2["pre"], ffn.w))
     _coef(pre2, ref2["pre"], CHAIN_COEF_ABS, "pre ffn (chain)")
     _coef(post2, ref2["post"], CHAIN_COEF_ABS, "post ffn (chain)")
     _coef(comb2, ref2["comb"], CHAIN_COEF_ABS, "comb ffn (chain)")
@@ -102,7 +104,8 @@ def test_config4_prefill_chunk_post_pre_mxfp8(sites):
     ridx = torch.from_numpy(rows).to(gu.DEV)
     gu.assert_coef_close(gu.f32_np(comb0[ridx]), ref0["comb"], "comb attn (setup)")
     gu.assert_bf16_close(gu.bits_of(R1[ridx]), oR1, "R' after post")
-    gu.assert_bf16_close(gu.bits_of(y[ridx]), ref2["y"], "y ffn")
+    gu.assert_bf16_close(gu.bits_of(y[ridx]), ref2["y"], "y ffn",
+                         extra=gu.chain_y_slack(oR1_bits, ref2["pre"], ffn.w))
     _coef(comb2[ridx], ref2["comb"], CHAIN_COEF_ABS, "comb ffn (chain)")
     # the ffn pre against the oracle's pre of the GPU's own R' bits: per-stage bars
     ref2g = ffn.oracle_pre(gu.bits_of(R1[ridx]))

@@ -286,10 +286,11 @@ def test_fused_post_pre_matches_oracle(attn, ffn):
         gu.assert_coef_close(gu.f32_np(g), ref2g[name], f"{name} ffn")
     # and against the oracle's whole chain (its own R'), one bf16 rounding of R' apart
     ref2 = ffn.oracle_pre(oR1_bits)
-    gu.assert_bf16_close(gu.bits_of(y), ref2["y"], "y ffn (oracle chain)")
+    gu.assert_bf16_close(gu.bits_of(y), ref2["y"], "y ffn (oracle chain)",
+                         extra=gu.chain_y_slack(oR1_bits, ref2["pre"], ffn.w))
     for name, g in (("pre", pre2), ("post", post2), ("comb", comb2)):
         err = np.abs(gu.f32_np(g) - ref2[name]).max()
-        assert err <= 2e-3, f"{name} ffn (oracle chain): {err}"
+        assert err <= gu.CHAIN_COEF_ABS, f"{name} ffn (oracle chain): {err}"
 
 
 @pytest.mark.parametrize("M", [65, 4096])
@@ -555,14 +556,13 @@ def test_padded_row_strides_fused_and_separate(attn, ffn):
     assert torch.equal(Rb, Rb0) and torch.equal(xb, xb0)  # inputs, pads included, untouched
 
 
-def test_full_size_post_pre_matches_oracle_on_sampled_rows(attn, ffn):
+def test_full_size_post_pre_matches_oracle_on_every_row(attn, ffn):
     """The measured step itself: hc_post_pre at M = 4096, H = 5120 in the launch the throughput
     benchmark times (256 blocks, 16 per column slice, each running 16 stages of one 16-row
-    group), against the oracle's post followed by its pre on sampled rows: every row group's
-    first and last row, the first and last 70 rows, and 200 drawn at random. post and comb come
+    group), against the oracle's post followed by its pre on all 4096 rows. post and comb come
     from the oracle's pre of the attention site."""
     M = 4096
-    gu.say(f"hc_post_pre full size M={M} sampled")
+    gu.say(f"hc_post_pre full size M={M} every row")
     R = inputs.residual(M, 4096 + 11)
     x = inputs.sublayer_out(M, 4096 + 12)
     ref1 = attn.oracle_pre(inputs.bits(R))
@@ -573,26 +573,25 @@ def test_full_size_post_pre_matches_oracle_on_sampled_rows(attn, ffn):
         ffn.base_d, ffn.w_d, want_pre=True,
         out=(_poison_bf16(M, 4, gu.H), _poison_bf16(M, gu.H), _poison_f32(M, 4),
              _poison_f32(M, 4, 4), _poison_f32(M, 4)))
-    rng = np.random.default_rng(4096)
-    edges = np.concatenate([np.arange(0, M, 16), np.arange(15, M, 16)])
-    rows = np.unique(np.concatenate([edges, np.arange(70), np.arange(M - 70, M),
-                                     rng.choice(M, 200, replace=False)]))
-    oR1, oR1_bits = o.hc_post(inputs.bits(x)[rows], inputs.bits(R)[rows], post32.numpy()[rows],
-                              comb32.numpy()[rows])
-    ridx = torch.from_numpy(rows).to(gu.DEV)
-    gRn = gu.bits_of(Rn[ridx])
-    gu.assert_bf16_close(gRn, oR1, "R' (sampled)")
-    # the pre half on the GPU's own R' bits of those rows: per-stage bars (coefficients 1e-5)
+    oR1, oR1_bits = o.hc_post(inputs.bits(x), inputs.bits(R), post32.numpy(), comb32.numpy())
+    gRn = gu.bits_of(Rn)
+    gu.assert_bf16_close(gRn, oR1, "R'")
+    del oR1
+    # the pre half on the GPU's own R' bits: per-stage bars (coefficients 1e-5)
     ref2g = ffn.oracle_pre(gRn)
-    gu.assert_bf16_close(gu.bits_of(y[ridx]), ref2g["y"], "y (sampled)")
+    gy = gu.bits_of(y)
+    gu.assert_bf16_close(gy, ref2g["y"], "y")
     for name, g in (("pre", pre2), ("post", post2), ("comb", comb2)):
-        gu.assert_coef_close(gu.f32_np(g[ridx]), ref2g[name], f"{name} (sampled)")
-    # and against the oracle's whole chain (its own R'), one bf16 rounding of R' apart
+        gu.assert_coef_close(gu.f32_np(g), ref2g[name], name)
+    del ref2g
+    # and against the oracle's whole chain (its own R'), one bf16 rounding of R' apart: y also
+    # moves by what that rounding and the 2e-3 coefficient bar can shift where the combine cancels
     ref2 = ffn.oracle_pre(oR1_bits)
-    gu.assert_bf16_close(gu.bits_of(y[ridx]), ref2["y"], "y (sampled, oracle chain)")
+    gu.assert_bf16_close(gy, ref2["y"], "y (oracle chain)",
+                         extra=gu.chain_y_slack(oR1_bits, ref2["pre"], ffn.w))
     for name, g in (("pre", pre2), ("post", post2), ("comb", comb2)):
-        err = np.abs(gu.f32_np(g[ridx]) - ref2[name]).max()
-        assert err <= 2e-3, f"{name} (sampled, oracle chain): {err}"
-    # properties that hold at any size, on all 4096 rows
+        err = np.abs(gu.f32_np(g) - ref2[name]).max()
+        assert err <= gu.CHAIN_COEF_ABS, f"{name} (oracle chain): {err}"
+    # properties that hold at any size
     gu.assert_coef_properties(pre2, post2, comb2)
     assert torch.isfinite(y.float()).all() and torch.isfinite(Rn.float()).all()
