@@ -556,6 +556,65 @@ def test_padded_row_strides_fused_and_separate(attn, ffn):
     assert torch.equal(Rb, Rb0) and torch.equal(xb, xb0)  # inputs, pads included, untouched
 
 
+def test_rows_past_32_bit_offsets(attn, ffn):
+    """M = 131072 rows at H = 5120: R takes 5.4 GB, so row offsets pass 2^31 bytes (from row
+    52429) and 2^31 elements (from row 104858). The batch is 32 copies of one seeded 4096-row
+    block, copy k rolled by 37 k rows, so an address that wraps or truncates reads a row other
+    than the one its output stands for. Every entry point's outputs for copy k must equal those
+    of the block alone rolled the same way, bit for bit: the fused step, post then pre, the
+    MXFP8 form with the quantizer, and the head. (The block's own parity with the oracle is the
+    full-size test below.)"""
+    B, K = 4096, 32
+    M = B * K
+    assert M * 4 * gu.H > 2**31
+    gu.say(f"rows past 32-bit offsets M={M}")
+    shifts = [37 * k for k in range(K)]
+
+    def tile(t):
+        return torch.cat([torch.roll(t, sh, dims=0) for sh in shifts])
+
+    def check(big, small, what):
+        if big.dtype == torch.bfloat16:
+            big, small = big.view(torch.int16), small.view(torch.int16)
+        for k, sh in enumerate(shifts):
+            assert torch.equal(big[k * B:(k + 1) * B], torch.roll(small, sh, dims=0)), \
+                f"{what}: copy {k} (rows {k * B}..{(k + 1) * B - 1})"
+
+    R0 = gu.dev(inputs.residual(B, 4096 + 11))
+    x0 = gu.dev(inputs.sublayer_out(B, 4096 + 12))
+    _, p0, c0, _ = ops.pre(R0, attn.fnp, attn.scale_d, attn.base_d, attn.w_d)
+    small = ops.post_pre(x0, R0, p0, c0, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d,
+                         want_pre=True)
+    R, x, post_, comb = tile(R0), tile(x0), tile(p0), tile(c0)
+    full = ops.post_pre(x, R, post_, comb, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d,
+                        want_pre=True)
+    for what, big, sm in zip(("R'", "y", "post", "comb", "pre"), full, small):
+        check(big, sm, f"hc_post_pre {what}")
+    # post then pre on the same batch: the fused op's bits
+    Rn = ops.post(x, R, post_, comb)
+    assert torch.equal(Rn.view(torch.int16), full[0].view(torch.int16))
+    y2, post2, comb2, _ = ops.pre(Rn, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d)
+    assert torch.equal(y2.view(torch.int16), full[1].view(torch.int16))
+    assert torch.equal(post2, full[2]) and torch.equal(comb2, full[3])
+    del Rn, y2, post2, comb2
+    # the MXFP8 form and the quantizer over the whole batch
+    Rq, (yq, q, sf, _, _, _) = ops.post_pre_mxfp8(x, R, post_, comb, ffn.fnp, ffn.scale_d,
+                                                  ffn.base_d, ffn.w_d)
+    assert torch.equal(Rq.view(torch.int16), full[0].view(torch.int16))
+    assert torch.equal(yq.view(torch.int16), full[1].view(torch.int16))
+    del Rq, yq
+    q0, sf0 = ops.mxfp8_quant_rows(small[1])
+    check(q, q0, "q")
+    check(sf, sf0, "scales")
+    q2, sf2 = ops.mxfp8_quant_rows(full[1])
+    assert torch.equal(q2, q) and torch.equal(sf2, sf)
+    del q, sf, q2, sf2, full, x, post_, comb
+    # the head over the same residual
+    hf, hs, hb = inputs.hc_head_params(inputs.SEED_HEAD)
+    hfp, hs_d, hb_d = ops.head_fn_pack(gu.dev(hf)), gu.dev(hs), gu.dev(hb)
+    check(ops.head(R, hfp, hs_d, hb_d), ops.head(R0, hfp, hs_d, hb_d), "head y")
+
+
 def test_full_size_post_pre_matches_oracle_on_every_row(attn, ffn):
     """The measured step itself: hc_post_pre at M = 4096, H = 5120 in the launch the throughput
     benchmark times (256 blocks, 16 per column slice, each running 16 stages of one 16-row
