@@ -87,6 +87,63 @@ def test_sinkhorn_matches_oracle(attn, M):
     gu.assert_coef_close(gu.f32_np(comb), ocomb, "comb")
 
 
+ARG_SETS = [  # iters, rms_eps, pre_eps, sinkhorn_eps, post_mult, norm_eps
+    (1, 1e-6, 1e-6, 1e-6, 2.0, 1e-6),
+    (2, 1e-4, 1e-3, 1e-5, 1.5, 1e-5),
+    (7, 0.0, 0.0, 0.0, 2.0, 1e-3),
+    (50, 1e-6, 1e-6, 1e-2, 2.0, 1e-6),
+]
+
+
+def _oracle_pre_args(site, R_bits, iters, rms_eps, pre_eps, sk_eps, post_mult, norm_eps):
+    mixes, _ = o.hc_mix_stats(R_bits, site.fn.numpy(), rms_eps)
+    pre, post, logits = o.hc_split(mixes, site.scale.numpy(), site.base.numpy(), pre_eps=pre_eps,
+                                   post_mult=post_mult)
+    comb = o.sinkhorn(logits, iters, sk_eps)
+    y, _ = o.hc_combine_norm(R_bits, pre, inputs.bits(site.w), norm_eps)
+    return dict(mixes=mixes, pre=pre, post=post, comb=comb, y=y)
+
+
+@pytest.mark.parametrize("args", ARG_SETS, ids=[f"iters{a[0]}" for a in ARG_SETS])
+def test_non_default_arguments_match_oracle(attn, ffn, args):
+    """Every argument the entry points take besides the tensors, away from the decoder layer's
+    values: 1, 2, 7 and 50 Sinkhorn rounds, pre and Sinkhorn eps that differ (zero included),
+    other rms / norm eps and post multipliers. hc_sinkhorn on the oracle's mixes, hc_pre, and
+    the pre half of hc_post_pre (on the GPU's own R'), each against the oracle's stages called
+    with the same values, M = 300 (19 row groups, the last one ragged)."""
+    iters, rms_eps, pre_eps, sk_eps, post_mult, norm_eps = args
+    M = 300
+    gu.say(f"non-default arguments {args} M={M}")
+    R = inputs.residual(M, 300 + iters)
+    ref = _oracle_pre_args(attn, inputs.bits(R), *args)
+    mixes32 = torch.from_numpy(ref["mixes"].astype(np.float32))
+    pre, post, comb = ops.sinkhorn(gu.dev(mixes32), attn.scale_d, attn.base_d, iters=iters,
+                                   pre_eps=pre_eps, sinkhorn_eps=sk_eps, post_mult=post_mult)
+    # the oracle on the same fp32 mixes the kernel read
+    opre, opost, ologits = o.hc_split(mixes32.numpy(), attn.scale.numpy(), attn.base.numpy(),
+                                      pre_eps=pre_eps, post_mult=post_mult)
+    gu.assert_coef_close(gu.f32_np(pre), opre, "sinkhorn pre")
+    gu.assert_coef_close(gu.f32_np(post), opost, "sinkhorn post")
+    gu.assert_coef_close(gu.f32_np(comb), o.sinkhorn(ologits, iters, sk_eps), "sinkhorn comb")
+    kw = dict(rms_eps=rms_eps, pre_eps=pre_eps, sinkhorn_eps=sk_eps, iters=iters,
+              post_mult=post_mult, norm_eps=norm_eps)
+    y, post1, comb1, pre1 = ops.pre(gu.dev(R), attn.fnp, attn.scale_d, attn.base_d, attn.w_d,
+                                    want_pre=True, **kw)
+    for name, g in (("pre", pre1), ("post", post1), ("comb", comb1)):
+        gu.assert_coef_close(gu.f32_np(g), ref[name], f"hc_pre {name}")
+    gu.assert_bf16_close(gu.bits_of(y), ref["y"], "hc_pre y")
+    x = inputs.sublayer_out(M, 301 + iters)
+    Rn, y2, post2, comb2, pre2 = ops.post_pre(gu.dev(x), gu.dev(R), post1, comb1, ffn.fnp,
+                                              ffn.scale_d, ffn.base_d, ffn.w_d, want_pre=True,
+                                              **kw)
+    oR, _ = o.hc_post(inputs.bits(x), inputs.bits(R), gu.f32_np(post1), gu.f32_np(comb1))
+    gu.assert_bf16_close(gu.bits_of(Rn), oR, "hc_post_pre R'")
+    ref2 = _oracle_pre_args(ffn, gu.bits_of(Rn), *args)
+    for name, g in (("pre", pre2), ("post", post2), ("comb", comb2)):
+        gu.assert_coef_close(gu.f32_np(g), ref2[name], f"hc_post_pre {name}")
+    gu.assert_bf16_close(gu.bits_of(y2), ref2["y"], "hc_post_pre y")
+
+
 @pytest.mark.parametrize("M", [1, 130, 1500])
 def test_combine_norm_matches_oracle(attn, M):
     gu.say(f"hc_combine_norm M={M}")
