@@ -3,7 +3,8 @@
 // mhc_fused_post_pre, which takes the previous sublayer's hc post together with the next
 // hc pre). Per row x (flattened stream-major, 4H values) the kernel produces, for each of S
 // column slices, the partial dots d[f] = sum_k fn[f, k] x_k (24 of them) and sum_k x_k^2.
-// In the fused form x is the bf16 R' = post * y + comb^T R that the kernel also stores.
+// In the fused form the row is R' = post * x + comb^T R (x the sublayer output, one bf16
+// rounding), which the kernel also stores.
 //
 // Arithmetic: the 24 x 4H projection runs on the matrix cores (v_mfma_f32_16x16x32_bf16).
 // x is exactly bf16; fn is fp32, split once per weight into three bf16 parts hi + mid + lo
