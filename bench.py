@@ -19,7 +19,8 @@ K back-to-back launches on the rotating input sets between one pair of HIP event
 the stream it runs on, divided by K. The roofline's "traffic" is the HBM byte count that
 rocprofv3's FETCH_SIZE / WRITE_SIZE counters gave for that kernel; it is read from the summary
 under profiles/ and reported only while the kernel's source files still hash to what that
-summary records (null otherwise).
+summary records (null otherwise). "traffic_gbps" is that byte count over the same
+back-to-back duration.
 
 --workload config3 / config4 time the other two chained workloads instead (one JSON line
 each, no CPU baseline): the M = 1500 chain pre(attn) -> post -> pre(ffn), and the M = 16384
@@ -365,6 +366,7 @@ def chain_workload(args, torch, ops, inputs, d) -> int:
     kname, _, kfiles = ROOFLINE_KERNEL["fused"]
     kbytes = M * POST_BYTES_ROW + FN_BYTES
     gbs = nbytes / (ms * 1e-3) / 1e9
+    traffic = recorded_traffic(kname, kfiles, M)
     print(json.dumps({
         "workload": args.workload, "M": M, "H": H, "steps": args.steps, "warmup": args.warmup,
         "desc": wl["desc"], "ms_per_step": ms, "rows_per_s": M / (ms * 1e-3),
@@ -375,7 +377,8 @@ def chain_workload(args, torch, ops, inputs, d) -> int:
                      "ms": kms, "achieved": kbytes / (kms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": kbytes / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "algorithmic_bytes": kbytes,
-                     "traffic": recorded_traffic(kname, kfiles, M),
+                     "traffic": traffic,
+                     "traffic_gbps": traffic / (kms * 1e-3) / 1e9 if traffic else None,
                      "source": kernel_source_hash(kfiles)},
         "input_sets": len(sets),
     }), flush=True)
@@ -519,6 +522,7 @@ def main() -> int:
                       "hc_pre (stats_kernel<10,false> + pre_finish_kernel)": second_ms}
     rows_s = M / (ms_step * 1e-3)
     step_gbs = STEP_BYTES / (ms_step * 1e-3) / 1e9
+    traffic = recorded_traffic(kname, kfiles)
     result = {
         "metric": "mHC pre+post rows/s and achieved HBM GB/s at M=4096, H=5120 (1 MI355X)",
         "value": rows_s,
@@ -555,7 +559,9 @@ def main() -> int:
             "unit": "GB/s",
             "frac": k_gbs / PEAK_HBM_GBS,
             "algorithmic_bytes": kbytes,
-            "traffic": recorded_traffic(kname, kfiles),
+            "traffic": traffic,
+            # the counted HBM bytes over the same back-to-back duration (null with traffic)
+            "traffic_gbps": traffic / (first_ms * 1e-3) / 1e9 if traffic else None,
             "source": kernel_source_hash(kfiles),
         },
     }
