@@ -1,5 +1,5 @@
 // Host-side launchers of the gfx950 kernels. Each returns the hipError_t of the launch; the
-// C-ABI layer (hc_api.cpp) validates every argument before calling them.
+// C-ABI layer (hc_api.hip) validates every argument before calling them.
 #pragma once
 
 #include <hip/hip_runtime.h>

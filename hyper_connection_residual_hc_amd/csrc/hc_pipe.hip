@@ -159,13 +159,11 @@ __global__ __launch_bounds__(512) void stats_kernel(PipeArgs a) {
   constexpr int W = 32 * NC;          // slice width (columns of each stream)
   constexpr int UR = W / 8;           // 16-byte units of one stream's slice of a row
   constexpr int UPR = kHC * UR;       // units of one LDS row (four streams)
-  constexpr int kWaveItems = UR / 4;  // per producer wave: 16 rows x UR units / 4 waves / 64
   constexpr int kFull = NC / 4;       // full wave-wide items
   constexpr bool kHalf = (NC % 4) != 0;  // plus one item in lanes 0-31 (NC % 4 == 2)
   constexpr int kItems = kFull + (kHalf ? 1 : 0);
   constexpr int kLoads = kPost ? kHC + 1 : kHC;
   static_assert(NC % 2 == 0 && NC >= 2 && NC <= 10, "slice geometry");
-  (void)kWaveItems;
 
   __shared__ __attribute__((aligned(16))) u32x4 ring[2][kGroupRows * UPR];
   __shared__ __attribute__((aligned(16))) float epi[2][kHC][kGroupRows][kEpiCols];
