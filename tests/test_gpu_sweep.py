@@ -1,0 +1,92 @@
+"""A seeded sweep over shape combinations no single test pins: hidden size, row count, row
+strides and where the rows start inside a larger buffer, all drawn at once. Each case checks
+the fused post -> pre against post then pre bit for bit, its MXFP8 form against the quantizer
+of its own y, and the first, the last and a few random rows against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from hyper_connection_residual_hc_amd import inputs, ops
+from oracle import hc_oracle as o
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+WIDTHS = [1024, 2048, 3072, 4096, 5120, 6144, 7168, 8192]
+
+
+def _cases(n):
+    rng = np.random.default_rng(2026)
+    out = []
+    for i in range(n):
+        H = int(rng.choice(WIDTHS))
+        M = int(np.exp(rng.uniform(0.0, np.log(3000.0))))
+        pad_r = int(rng.choice([0, 8, 64, 520]))  # elements; multiples of 8 keep 16-byte rows
+        pad_x = int(rng.choice([0, 8, 96]))
+        off = int(rng.integers(0, 5))  # rows of the buffer before the view starts
+        out.append((i, H, M, pad_r, pad_x, off))
+    return out
+
+
+CASES = _cases(16)
+
+
+def _view(t2d, pad, off, fill=-7.0):
+    """t2d [M, C] copied into rows off .. off + M of a [off + M, C + pad] buffer; the view."""
+    M, C = t2d.shape
+    buf = torch.full((off + M, C + pad), fill, dtype=t2d.dtype, device=gu.DEV)
+    v = buf[off:, :C]
+    v.copy_(t2d)
+    return buf, v
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"c{c[0]}-H{c[1]}-M{c[2]}")
+def test_shape_sweep(case):
+    i, H, M, pad_r, pad_x, off = case
+    gu.say(f"sweep case {i}: H={H} M={M} pad_r={pad_r} pad_x={pad_x} off={off}")
+    attn = gu.Site(700 + 4 * i, 701 + 4 * i, H_=H)
+    ffn = gu.Site(702 + 4 * i, 703 + 4 * i, H_=H)
+    R = inputs.residual(M, 800 + i, H=H)
+    x = inputs.sublayer_out(M, 900 + i, H=H)
+    Rd, xd = gu.dev(R), gu.dev(x)
+    Rbuf, Rv = _view(Rd.reshape(M, 4 * H), pad_r, off)
+    xbuf, xv = _view(xd, pad_x, off)
+    Rs = Rv.view(M, 4, H)
+    Rbuf0, xbuf0 = Rbuf.clone(), xbuf.clone()
+
+    y1, post1, comb1, pre1 = ops.pre(Rs, attn.fnp, attn.scale_d, attn.base_d, attn.w_d,
+                                     want_pre=True)
+    full = ops.post_pre(xv, Rs, post1, comb1, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d,
+                        want_pre=True)
+    Rn = ops.post(xd, Rd, post1, comb1)
+    y2, post2, comb2, pre2 = ops.pre(Rn, ffn.fnp, ffn.scale_d, ffn.base_d, ffn.w_d,
+                                     want_pre=True)
+    assert torch.equal(full[0].view(torch.int16), Rn.view(torch.int16))
+    assert torch.equal(full[1].view(torch.int16), y2.view(torch.int16))
+    for a, b in zip(full[2:], (post2, comb2, pre2)):
+        assert torch.equal(a, b)
+    Rq, (yq, q, sf, postq, combq, _) = ops.post_pre_mxfp8(xv, Rs, post1, comb1, ffn.fnp,
+                                                          ffn.scale_d, ffn.base_d, ffn.w_d)
+    assert torch.equal(Rq.view(torch.int16), Rn.view(torch.int16))
+    assert torch.equal(yq.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(postq, post2) and torch.equal(combq, comb2)
+    q0, sf0 = ops.mxfp8_quant_rows(y2)
+    assert torch.equal(q, q0) and torch.equal(sf, sf0)
+    assert torch.equal(Rbuf, Rbuf0) and torch.equal(xbuf, xbuf0)  # inputs and pads untouched
+
+    rng = np.random.default_rng(i)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 3)]))
+    ridx = torch.from_numpy(rows).to(gu.DEV)
+    ref1 = attn.oracle_pre(inputs.bits(R)[rows])
+    for name, g in (("pre", pre1), ("post", post1), ("comb", comb1)):
+        gu.assert_coef_close(gu.f32_np(g[ridx]), ref1[name], f"attn {name}")
+    gu.assert_bf16_close(gu.bits_of(y1[ridx]), ref1["y"], "attn y")
+    oR, _ = o.hc_post(inputs.bits(x)[rows], inputs.bits(R)[rows], gu.f32_np(post1)[rows],
+                      gu.f32_np(comb1)[rows])
+    gRn = gu.bits_of(Rn[ridx])
+    gu.assert_bf16_close(gRn, oR, "R'")
+    ref2 = ffn.oracle_pre(gRn)
+    for name, g in (("pre", pre2), ("post", post2), ("comb", comb2)):
+        gu.assert_coef_close(gu.f32_np(g[ridx]), ref2[name], f"ffn {name}")
+    gu.assert_bf16_close(gu.bits_of(y2[ridx]), ref2["y"], "ffn y")
+    gu.assert_coef_properties(pre2, post2, comb2)
