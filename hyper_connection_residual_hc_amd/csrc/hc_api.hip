@@ -39,7 +39,7 @@ int launched(hipError_t err) { return err == hipSuccess ? HC_OK : HC_ERR_LAUNCH;
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-bool stats_h_ok(int32_t H) { return hc::stats_geom(H).S > 0; }  // H = 1024 n <= 8192
+bool stats_h_ok(int32_t H) { return hc::stats_geom(H).S > 0; }  // 512 n <= 8192 but 5632, 6656
 bool post_h_ok(int32_t H) { return H > 0 && H % 512 == 0 && H <= (1 << 20); }
 
 // Row strides stay below 2^26 elements (the stats kernels address 16 rows of any array with

@@ -12,18 +12,20 @@ namespace hc {
 // Stats split-K geometry. The 4H columns of a flattened row split into S column slices: slice s
 // covers columns [s W, (s + 1) W) of every stream, W = H / S = 32 NC (NC MFMA chunks of 32
 // columns per stream). NC is the largest even value up to 10 with S = H / (32 NC) a multiple of
-// 4 and at least 8: a stats block keeps its slice's whole packed fn (NC chunks x 5 B-operand
-// tiles per stream, 20 NC registers per lane) in the registers of four MFMA waves, so the slice
-// must stay narrow; the stats kernels need H a multiple of 1024 and at most 8192.
-//   H:  1024 2048 3072 4096 5120 6144 7168 8192
-//   NC:    4    8    8    8   10    8    8    8
-//   S:     8    8   12   16   16   24   28   32
+// 4 from 8 to kMaxSlices: a stats block keeps its slice's whole packed fn (NC chunks x 5
+// B-operand tiles per stream, 20 NC registers per lane) in the registers of four MFMA waves, so
+// the slice must stay narrow. The stats kernels take every multiple of 512 up to 8192 that has
+// such an NC, which is all of them but 5632 and 6656:
+//   H:   512 1024 1536 2048 2560 3072 3584 4096 4608 5120 6144 7168 7680 8192
+//   NC:    2    4    6    8   10    8    4    8    6   10    8    8   10    8
+//   S:     8    8    8    8    8   12   28   16   24   16   24   28   24   32
 // Each (slice, row) gets a partial record of kPartStride floats: the 24 partial dots of that
 // slice's columns and their partial sum of squares.
 constexpr int kPackTiles = 5;         // B-operand tiles of 16 packed (part, fn row) columns
 constexpr int kGroupRows = 16;        // rows of one MFMA row tile (a stats row group)
 constexpr int kPartStride = 25;       // floats per (slice, row) partial record: 24 dots + sumsq
 constexpr int kMaxStatsH = 8192;
+constexpr int kMaxSlices = 32;  // the slice sums below hold up to this many records per row
 
 struct StatsGeom {
   int S;   // column slices
@@ -32,11 +34,11 @@ struct StatsGeom {
 };
 __host__ __device__ inline StatsGeom stats_geom(int H) {
   StatsGeom g{0, 0, 0};
-  if (H <= 0 || H % 1024 || H > kMaxStatsH) return g;
+  if (H <= 0 || H % 512 || H > kMaxStatsH) return g;
   for (int nc = 10; nc >= 2; nc -= 2) {
     if (H % (32 * nc)) continue;
     const int S = H / (32 * nc);
-    if (S % 4 || S < 8) continue;
+    if (S % 4 || S < 8 || S > kMaxSlices) continue;
     g.S = S;
     g.NC = nc;
     g.W = 32 * nc;
@@ -54,7 +56,6 @@ inline size_t stats_workspace_bytes(int64_t M, int H) {
 // (g = 0..3, slices in increasing order), then (t_0 + t_1) + (t_2 + t_3). S is a multiple of 4,
 // at most kMaxSlices. Every value is loaded before the first add (addresses clamped to the last
 // slice, extra values unused), so the loads overlap.
-constexpr int kMaxSlices = 32;
 constexpr int kMaxSliceRounds = kMaxSlices / 4;
 __device__ __forceinline__ const float* part_at(const float* part, int M, int s, int m, int f) {
   return part + ((int64_t)s * M + m) * kPartStride + f;

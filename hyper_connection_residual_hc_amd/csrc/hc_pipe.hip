@@ -436,7 +436,9 @@ static hipError_t launch_pipe(bool fused, PipeArgs args, hipStream_t s) {
       hipLaunchKernelGGL((stats_kernel<nc, false>), grid, block, 0, s, args);                    \
     break;
   switch (geo.NC) {
+    HC_STATS_CASE(2)
     HC_STATS_CASE(4)
+    HC_STATS_CASE(6)
     HC_STATS_CASE(8)
     HC_STATS_CASE(10)
     default: return hipErrorInvalidValue;

@@ -70,7 +70,8 @@ HC_API int hc_abi_version(void);
  *
  * fn:        fp32 [24, 4H] row-major (device).
  * fn_packed: hc_fn_packed_bytes(H) bytes (device, 16-byte aligned), written.
- * H:         multiple of 1024, at most 8192.
+ * H:         a multiple of 512 up to 8192, except 5632 and 6656 (HC_ERR_SHAPE; the column
+ *            slices the stats kernel needs do not divide them).
  * ------------------------------------------------------------------------------------- */
 HC_API size_t hc_fn_packed_bytes(int32_t H);
 HC_API int hc_fn_pack(const float* fn, int32_t H, uint16_t* fn_packed, void* stream);
@@ -86,7 +87,7 @@ HC_API int hc_fn_pack(const float* fn, int32_t H, uint16_t* fn_packed, void* str
  * sumsq:      fp32 [M] or NULL, written when given.
  * workspace:  >= hc_pre_stats_workspace_bytes(M, H) bytes of device memory, 256-byte aligned;
  *             its contents on entry do not matter.
- * H:          multiple of 1024, at most 8192.
+ * H:          as hc_fn_pack.
  * ------------------------------------------------------------------------------------- */
 HC_API size_t hc_pre_stats_workspace_bytes(int64_t M, int32_t H);
 HC_API int hc_pre_stats(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed, int64_t M,
@@ -159,8 +160,8 @@ HC_API int mxfp8_quant_rows(const uint16_t* y, int64_t ldY, int64_t M, int32_t K
  * hc_pre_stats -> hc_sinkhorn -> hc_combine_norm.
  *
  * pre may be NULL (not written); post fp32 [M, 4], comb fp32 [M, 4, 4], y bf16 [M, H] (ldY).
- * H: as hc_combine_norm and a multiple of 1024. workspace: >= hc_pre_workspace_bytes(M, H),
- * 256-byte aligned (HC_ERR_ALIGN otherwise).
+ * H: as hc_fn_pack (every such H is one hc_combine_norm takes). workspace: >=
+ * hc_pre_workspace_bytes(M, H), 256-byte aligned (HC_ERR_ALIGN otherwise).
  * ------------------------------------------------------------------------------------- */
 HC_API size_t hc_pre_workspace_bytes(int64_t M, int32_t H);
 HC_API int hc_pre(const uint16_t* R, int64_t ldR, const uint16_t* fn_packed,

@@ -44,12 +44,18 @@ def test_status_strings(L):
 def test_sizes(L):
     H = 5120
     assert L.hc_fn_packed_bytes(H) == 8 * (4 * (H // 8) // 32) * 5 * 64 * 8 * 2
-    assert L.hc_fn_packed_bytes(512) == 0  # stats need a multiple of 1024
+    assert L.hc_fn_packed_bytes(512) == 4 * 512 * 5 * 16 * 2
+    assert L.hc_fn_packed_bytes(5632) == 0  # no slice count fits 5632 or 6656
+    assert L.hc_fn_packed_bytes(6656) == 0
+    assert L.hc_fn_packed_bytes(1000) == 0
     assert L.hc_fn_packed_bytes(100) == 0
     # partial records: 16 slices x 25 floats per row at H = 5120; 28 slices at 7168
     assert L.hc_pre_stats_workspace_bytes(4096, H) == 16 * 4096 * 25 * 4
     assert L.hc_pre_stats_workspace_bytes(10, 7168) == 28 * 10 * 25 * 4
     assert L.hc_pre_stats_workspace_bytes(10, 9216) == 0  # the stats stop at 8192
+    # slices at the odd multiples of 512: 8 at 512, 1536, 2560; 28 at 3584; 24 at 4608, 7680
+    for Hs, S in ((512, 8), (1536, 8), (2560, 8), (3584, 28), (4608, 24), (7680, 24)):
+        assert L.hc_pre_stats_workspace_bytes(10, Hs) == S * 10 * 25 * 4
     assert L.hc_pre_workspace_bytes(0, H) == 0
     assert L.hc_pre_stats_workspace_bytes(-1, H) == 0
 
@@ -99,7 +105,7 @@ def test_validation_codes_of_the_post_pre_halves(L):
     # NULL, shape, workspace, alias
     assert L.hc_post_stats(None, H, fake, 4 * H, fake, fake, fake, 7, H, fake, 4 * H, ws, need,
                            None) == 1
-    assert L.hc_post_stats(a, H, b, 4 * H, c, c, d, 7, 512 * 3, fake, 4 * H, ws, need, None) == 2
+    assert L.hc_post_stats(a, H, b, 4 * H, c, c, d, 7, 512 * 11, fake, 4 * H, ws, need, None) == 2
     assert L.hc_post_stats(a, H, b, 4 * H, c, c, d, 7, H, fake, 4 * H, ws, need - 4, None) == 5
     assert L.hc_post_stats(a, H, b, 4 * H, c, ctypes.c_void_p(0x3000040), d, 7, H, b, 4 * H, ws,
                            need, None) == 4

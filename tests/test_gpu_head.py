@@ -77,11 +77,11 @@ def test_head_zero_scale_and_slices(head):
         assert torch.equal(part.view(torch.int16), full[lo:hi].view(torch.int16)), (lo, hi)
 
 
-@pytest.mark.parametrize("Hs,M", [(3072, 130), (6144, 70), (1024, 1100)])
+@pytest.mark.parametrize("Hs,M", [(3072, 130), (6144, 70), (1024, 1100), (2560, 90), (7680, 40)])
 def test_head_other_widths(Hs, M):
-    """Other row widths against the oracle: 6 and 12 column blocks per lane in the head's
-    finish, and at H = 1024 the stats kernel's narrowest geometry (8 slices of 128 columns per
-    stream, 32 blocks per slice running 2 or 3 stages at 1100 rows)."""
+    """Other row widths against the oracle: 5 to 15 column blocks per lane in the head's
+    finish, at H = 1024 8 slices of 128 columns per stream (32 blocks per slice running 2 or 3
+    stages at 1100 rows), and the odd multiples 2560 and 7680 (NC = 10, 8 and 24 slices)."""
     gu.say(f"hc_head H={Hs} M={M}")
     fn, scale, base = inputs.hc_head_params(inputs.SEED_HEAD + 1, H=Hs)
     R = inputs.residual(M, M + 7, H=Hs)

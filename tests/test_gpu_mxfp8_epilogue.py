@@ -99,7 +99,7 @@ def test_pre_mxfp8_row_slices_are_bit_identical(sites):
             assert _bits_equal(part[k], full[k][lo:hi]), (k, lo, hi)
 
 
-@pytest.mark.parametrize("Hs,M", [(1024, 70), (3072, 33), (6144, 130), (8192, 17)])
+@pytest.mark.parametrize("Hs,M", [(1024, 70), (1536, 50), (3072, 33), (4608, 21), (6144, 130), (8192, 17)])
 def test_mxfp8_epilogue_at_other_widths(Hs, M):
     """The finish's MXFP8 epilogue compiled for other row widths (2 to 16 column blocks of 512
     per lane; 32 to 256 scale blocks per row): the fused pre and the fused post -> pre give

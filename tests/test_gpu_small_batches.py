@@ -28,7 +28,7 @@ def _eq(a, b):
     return torch.equal(a, b)
 
 
-@pytest.mark.parametrize("H", [5120, 1024, 2048, 3072, 4096, 6144, 7168, 8192])
+@pytest.mark.parametrize("H", [5120, 512, 1024, 2048, 3072, 3584, 4096, 4608, 6144, 7168, 8192])
 def test_small_batch_slices_match_the_full_call(H):
     gu.say(f"small-batch slices H={H}")
     attn = gu.Site(inputs.SEED_ATTN, inputs.SEED_NORM_ATTN, H_=H)

@@ -12,7 +12,7 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-WIDTHS = [1024, 2048, 3072, 4096, 5120, 6144, 7168, 8192]
+WIDTHS = [512, 1024, 1536, 2048, 2560, 3072, 3584, 4096, 4608, 5120, 6144, 7168, 7680, 8192]
 
 
 def _cases(n):
