@@ -273,7 +273,7 @@ def test_error_codes_reach_python(attn):
 
 
 def test_small_hidden_size():
-    """H = 1024: the smallest hidden size of the stats kernel (one 1 KB stage per slice row)
+    """H = 1024: 8 stats slices of 128 columns per stream (one 1 KB stage per slice row)
     and two column blocks per lane in the combine and post kernels."""
     Hs = 1024
     site = gu.Site(5, 6, H_=Hs)
@@ -460,8 +460,8 @@ def test_combine_norm_and_post_at_odd_block_counts(Hs):
             ops.fn_pack(gu.dev(inputs.hc_params(1, H=Hs)[0]))
 
 
-def test_narrowest_hidden_size_two_stages_per_slice():
-    """H = 1024, the narrowest width with mix stats: 8 column slices of 128 columns per stream
+def test_narrow_hidden_size_two_stages_per_slice():
+    """H = 1024, a narrow width with mix stats: 8 column slices of 128 columns per stream
     (NC = 4, one full wave-wide item per array and producer wave), 32 blocks per slice. At
     M = 6161 (386 row groups, the last one ragged) the blocks run 12 or 13 stages each: the pre
     vs the oracle on sampled rows, and the fused op vs post then pre, bit for bit."""
