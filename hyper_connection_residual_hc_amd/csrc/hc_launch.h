@@ -32,7 +32,7 @@ struct StatsGeom {
   int NC;  // 32-column MFMA chunks of each stream in a slice
   int W;   // slice width (columns of each stream)
 };
-__host__ __device__ inline StatsGeom stats_geom(int H) {
+__host__ __device__ constexpr StatsGeom stats_geom(int H) {
   StatsGeom g{0, 0, 0};
   if (H <= 0 || H % 512 || H > kMaxStatsH) return g;
   for (int nc = 10; nc >= 2; nc -= 2) {
@@ -45,6 +45,11 @@ __host__ __device__ inline StatsGeom stats_geom(int H) {
     return g;
   }
   return g;
+}
+// Rounds of 4 slice records a row's partial sums take at width H (S / 4). Kernels compiled per
+// width size their sums with it; widths without mix stats get 1 so that they still compile.
+__host__ __device__ constexpr int slice_rounds(int H) {
+  return stats_geom(H).S > 0 ? stats_geom(H).S / 4 : 1;
 }
 inline int64_t packed_fn_elems(int H) { return (int64_t)4 * H * kPackTiles * 16; }
 inline size_t stats_workspace_bytes(int64_t M, int H) {
@@ -61,16 +66,18 @@ __device__ __forceinline__ const float* part_at(const float* part, int M, int s,
   return part + ((int64_t)s * M + m) * kPartStride + f;
 }
 // t_g of slice group g (the running sum over slices g, g + 4, ... < S)
+// (NR rounds: slice_rounds(H) in kernels compiled per width, kMaxSliceRounds otherwise)
+template <int NR>
 __device__ __forceinline__ void slice_group_load(const float* __restrict__ part, int S, int M,
-                                                 int m, int f, int g,
-                                                 float (&v)[kMaxSliceRounds]) {
+                                                 int m, int f, int g, float (&v)[NR]) {
 #pragma unroll
-  for (int j = 0; j < kMaxSliceRounds; ++j) v[j] = *part_at(part, M, min(4 * j + g, S - 1), m, f);
+  for (int j = 0; j < NR; ++j) v[j] = *part_at(part, M, min(4 * j + g, S - 1), m, f);
 }
-__device__ __forceinline__ float slice_group_sum(const float (&v)[kMaxSliceRounds], int S, int g) {
+template <int NR>
+__device__ __forceinline__ float slice_group_sum(const float (&v)[NR], int S, int g) {
   float t = v[0];
 #pragma unroll
-  for (int j = 1; j < kMaxSliceRounds; ++j)
+  for (int j = 1; j < NR; ++j)
     if (4 * j + g < S) t += v[j];
   return t;
 }

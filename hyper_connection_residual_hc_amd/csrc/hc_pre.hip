@@ -169,7 +169,8 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(
   // Loads in issue order: this lane's slice partials (its 16-lane group's quarter of the
   // slices), then the row. Vector loads complete in order, so the split + Sinkhorn waits only
   // for the partials and runs while the row is in flight.
-  float pa[kMaxSliceRounds], pc[kMaxSliceRounds], pq[kMaxSliceRounds];
+  constexpr int NR = slice_rounds(NG * 512);  // S / 4 at this width
+  float pa[NR], pc[NR], pq[NR];
   slice_group_load(part, S, M, m, e & 7, sg, pa);
   slice_group_load(part, S, M, m, 8 + e, sg, pc);
   slice_group_load(part, S, M, m, kMix, sg, pq);
@@ -220,7 +221,8 @@ __global__ __launch_bounds__(256) void head_finish_kernel(
   const int m = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
   if (m >= M) return;
   const int sg = lane >> 4;
-  float pd[kHC][kMaxSliceRounds], pq[kMaxSliceRounds];
+  constexpr int NR = slice_rounds(NG * 512);  // S / 4 at this width
+  float pd[kHC][NR], pq[NR];
 #pragma unroll
   for (int i = 0; i < kHC; ++i) slice_group_load(part, S, M, m, i, sg, pd[i]);
   slice_group_load(part, S, M, m, kMix, sg, pq);
